@@ -1,0 +1,162 @@
+/*
+ * clis.h -- C ABI of the CLiS attention-forward library for AMD MI355X (gfx950).
+ *
+ * CLiS (Certified Loop-invariant Stabilization) is described on the pages
+ * "CLiS: Plug-and-Play Attention Acceleration for Video Diffusion on TPUs via
+ * Certified Stabilization" (cited below as [CLiS ...]).  Per the abstract, it
+ * fixes each query row's softmax stabilizer before the key/value loop, so the
+ * loop needs no running maximum and no accumulator rescaling; it certifies
+ * per head that this is numerically safe, and heads that fail fall back to
+ * online softmax.  The output is ordinary softmax attention
+ *     O = softmax(scale * Q K^T [+ causal mask]) V
+ * so the library drops in where a fused attention forward was called.
+ *
+ * Layout.  Q [B, H, Nq, d], K and V [B, H, Nk, d], O [B, H, Nq, d]: dense,
+ * row-major, d innermost, one element type for all four (bf16 or fp32).
+ * Stabilizers mu [B, H, Nq] fp32, flags cert and routes [B, H] int32.
+ *
+ * Ownership.  The caller owns every buffer.  All pointers except `stream`
+ * are DEVICE pointers; q, k, v, o must be 16-byte aligned and ws 256-byte
+ * aligned.  The library never allocates or frees memory; scratch space comes
+ * from the caller's workspace `ws` of at least clis_workspace_bytes(...)
+ * bytes.  `stream` is a hipStream_t passed as void* (NULL: the null stream).
+ *
+ * Execution.  Every call only enqueues kernels on `stream` and returns; there
+ * is no host synchronisation and no device-to-host copy, also in auto mode,
+ * where each head's route is read on the device.  Results are valid once the
+ * stream has reached them, and are bitwise reproducible run to run (fixed
+ * reduction orders, no floating-point atomics).  Calls on distinct streams
+ * may overlap if their workspaces and outputs are disjoint.
+ *
+ * Errors.  Every entry point returns a clis_status_t.  A nonzero status means
+ * nothing was enqueued (except CLIS_ERR_HIP, which reports a failed launch);
+ * clis_last_error() then gives a thread-local description.  No C++ exception
+ * or abort crosses the ABI.
+ *
+ * Shapes.  d must be 64 or 128.  B, H, Nq may be 0 (nothing is enqueued and
+ * CLIS_OK is returned); a call with at least one query row needs Nk >= 1.
+ * causal needs Nq == Nk (query i sees keys 0..i).  scale must be finite and
+ * > 0.  Every dimension must fit in int32, and B*H*N*d in int64.
+ */
+#ifndef CLIS_H
+#define CLIS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { CLIS_BF16 = 0, CLIS_FP32 = 1 } clis_dtype_t;
+
+/* How clis_attn_fwd picks each head's kernel [CLiS abstract]. */
+typedef enum {
+  CLIS_MODE_AUTO = 0,   /* certified heads: fixed stabilizer; the rest: online softmax */
+  CLIS_MODE_FIXED = 1,  /* every head on the fixed-stabilizer kernel (testing tool: an
+                           uncertified head may overflow to Inf/NaN) */
+  CLIS_MODE_ONLINE = 2  /* every head on the online-softmax kernel */
+} clis_mode_t;
+
+typedef enum {
+  CLIS_OK = 0,
+  CLIS_ERR_NULL = 1,        /* a required pointer is NULL */
+  CLIS_ERR_SHAPE = 2,       /* bad dimension, scale, or causal with Nq != Nk */
+  CLIS_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, or unknown dtype / mode */
+  CLIS_ERR_ALIGN = 4,       /* q/k/v/o not 16-byte, or ws not 256-byte aligned */
+  CLIS_ERR_WORKSPACE = 5,   /* ws missing or smaller than clis_workspace_bytes() */
+  CLIS_ERR_HIP = 6          /* a HIP launch failed; see clis_last_error() */
+} clis_status_t;
+
+/* Per-head certification record, the quantities of [CLiS Algorithm 1]. */
+typedef struct {
+  double kappa;     /* step 3: max_r ||k_r - kbar||_2, fp64 */
+  double qnorm_max; /* max_r ||q_r||_2, fp64 */
+  double bound;     /* step 4: B_h = scale*log2(e) * qnorm_max * kappa */
+  double maxabs_v;  /* step 5: max |V| over the head */
+  int32_t G;        /* step 5: ceil(log2 max(1, maxabs_v)); 128 if non-finite */
+  int32_t L;        /* step 6: ceil(log2 Nk) */
+  int32_t A;        /* step 6: L + G */
+  int32_t C;        /* step 7: 127 - A */
+  int32_t cert;     /* 1 iff bound is finite and bound <= C */
+  int32_t reserved;
+} clis_head_stats_t;
+
+/* Workspace bytes any entry point of this library needs for these shapes
+ * (the certification scratch plus stabilizers, flags and route lists). */
+size_t clis_workspace_bytes(int B, int H, int Nq, int Nk, int d);
+
+/*
+ * Certify every (b, h) head and compute its fixed stabilizers
+ * [CLiS Algorithm 1, steps 1-7; abstract].  Per head, in fp64 with fixed
+ * reduction orders:
+ *   kbar = mean of the key rows;  kappa = max_r ||k_r - kbar||_2;
+ *   B_h = scale*log2(e) * max_r ||q_r||_2 * kappa  (Cauchy-Schwarz bound on
+ *         every exp2 argument scale*log2(e) * q.(k - kbar));
+ *   G = ceil(log2 max(1, max|V|)),  A = ceil(log2 Nk) + G,  C = 127 - A
+ *   (the exp2 and fp32-accumulator limits of [CLiS Figure 3]: floor(U_exp)
+ *   = 127 and ceil(U_acc - A) - 1 = 127 - A for fp32/bf16);
+ *   cert = B_h finite and B_h <= C;
+ *   mu_r = scale*log2(e) * (q_r . kbar), rounded to fp32 (log2 units).
+ * Inputs containing Inf or NaN make the head uncertified.
+ *   q, k, v    device inputs, layout above; dtype clis_dtype_t.
+ *   mu_out     device [B, H, Nq] fp32, required.
+ *   cert_out   device [B, H] int32, required (1 certified, 0 not).
+ *   stats_out  device [B, H] clis_head_stats_t, or NULL.
+ *   kbar_out   device [B, H, d] fp64, or NULL.
+ *   ws         device workspace of ws_bytes >= clis_workspace_bytes().
+ */
+int clis_certify(const void* q, const void* k, const void* v,
+                 int B, int H, int Nq, int Nk, int d, float scale, int dtype,
+                 float* mu_out, int32_t* cert_out, clis_head_stats_t* stats_out,
+                 double* kbar_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * CLiS attention forward [CLiS abstract; Figure 5(a)].  Heads routed to the
+ * fixed path evaluate, with no running maximum and no rescaling,
+ *   o_i = sum_j 2^{x_ij} v_j / sum_j 2^{x_ij},
+ *   x_ij = scale*log2(e) * (q_i . k_j) - mu_i,
+ * which equals softmax attention exactly in real arithmetic; heads routed to
+ * the online path run online softmax (the kernel of online_attn_fwd).
+ *   o          device output [B, H, Nq, d], same dtype as the inputs.
+ *   mode       clis_mode_t.
+ *   mu, cert   device results of clis_certify for these inputs, or NULL: if
+ *              the mode needs them (auto: both, fixed: mu) and either is NULL,
+ *              certification runs first inside this call, into ws.
+ *   route_out  device [B, H] int32 (1 fixed, 0 online), or NULL.
+ *   ws         device workspace (clis_workspace_bytes()); may be NULL only if
+ *              mode is online.
+ * Output dtype equals input dtype: fp32 accumulation, bf16 stored with round
+ * to nearest even; on the bf16 path the exp2 weights are rounded to bf16
+ * (nearest even) before the P.V product.
+ */
+int clis_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                  int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                  int mode, const float* mu, const int32_t* cert, int32_t* route_out,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Online-softmax attention forward for every head: the tuned baseline and the
+ * fallback path [CLiS abstract: running row maxima and accumulator
+ * rescaling].  Per key tile: m' = max(m, tile max of c*s), alpha = 2^{m-m'},
+ * l = alpha*l + sum 2^{c*s-m'}, O = alpha*O + P.V.  Bitwise equal to
+ * clis_attn_fwd with CLIS_MODE_ONLINE.  Needs no workspace.
+ */
+int online_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                    int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                    void* stream);
+
+/* Static text for a status code. */
+const char* clis_status_string(int status);
+
+/* Thread-local description of this thread's last failed call ("" if none). */
+const char* clis_last_error(void);
+
+/* ABI version of this header: 1. */
+int clis_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CLIS_H */

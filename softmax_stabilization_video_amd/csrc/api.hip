@@ -1,0 +1,208 @@
+// api.hip -- the C ABI of include/clis.h: argument checks, workspace carving,
+// routing and kernel launches.  Host code only; no allocation, no host
+// synchronisation, no device-to-host traffic.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(CLIS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape, scale and dtype checks shared by every entry point.  Returns
+// CLIS_OK, or an error status with the message set.  *empty is set when
+// there is no query row to compute (nothing should be enqueued).
+int check_common(int B, int H, int Nq, int Nk, int d, float scale, int dtype, int causal, bool* empty) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+    return fail(CLIS_ERR_SHAPE, "negative dimension (B=%d H=%d Nq=%d Nk=%d)", B, H, Nq, Nk);
+  if (dtype != CLIS_BF16 && dtype != CLIS_FP32) return fail(CLIS_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (d != 64 && d != 128) return fail(CLIS_ERR_UNSUPPORTED, "head dim %d not in {64, 128}", d);
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(CLIS_ERR_SHAPE, "scale must be finite and > 0");
+  if (causal && Nq != Nk) return fail(CLIS_ERR_SHAPE, "causal attention needs Nq == Nk (%d vs %d)", Nq, Nk);
+  *empty = (B == 0 || H == 0 || Nq == 0);
+  if (*empty) return CLIS_OK;
+  if (Nk < 1) return fail(CLIS_ERR_SHAPE, "Nk must be >= 1 when there are query rows");
+  const long long BH = (long long)B * H;
+  if (BH > 0x7fffffffLL) return fail(CLIS_ERR_SHAPE, "B*H exceeds int32");
+  const long long nmax = Nq > Nk ? Nq : Nk;
+  if (BH * nmax > (0x7fffffffffffffffLL / 4) / d) return fail(CLIS_ERR_SHAPE, "tensor too large");
+  return CLIS_OK;
+}
+
+int check_io(const void* q, const void* k, const void* v, const void* o, bool need_o) {
+  if (!q || !k || !v || (need_o && !o)) return fail(CLIS_ERR_NULL, "q, k, v%s must be non-NULL", need_o ? ", o" : "");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || (need_o && !aligned(o, 16)))
+    return fail(CLIS_ERR_ALIGN, "q, k, v, o must be 16-byte aligned");
+  return CLIS_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// Enqueue certification into caller buffers (workspace for the partials).
+int do_certify(const void* q, const void* k, const void* v, int B, int H, int Nq, int Nk, int d,
+               float scale, int dtype, float* mu, int32_t* cert, clis_head_stats_t* stats,
+               double* kbar, void* ws, hipStream_t s) {
+  const clis::WsLayout L = clis::ws_layout(B, H, Nq, Nk, d);
+  clis::CertifyArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.B = B; a.H = H; a.Nq = Nq; a.Nk = Nk; a.d = d;
+  a.scale = scale;
+  a.dtype = dtype;
+  a.mu = mu;
+  a.cert = cert;
+  a.stats = stats ? stats : at<clis_head_stats_t>(ws, L.stats);
+  a.kbar = kbar ? kbar : at<double>(ws, L.kbar);
+  a.ksum_part = at<double>(ws, L.ksum_part);
+  a.vmax_part = at<double>(ws, L.vmax_part);
+  a.kap_part = at<double>(ws, L.kap_part);
+  a.qss_part = at<double>(ws, L.qss_part);
+  const hipError_t e = clis::launch_certify(a, s);
+  if (e != hipSuccess) return hip_fail(e, "certify launch");
+  return CLIS_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, int B, int H, int Nq, int Nk, int d) {
+  if (!ws) return fail(CLIS_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(CLIS_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const size_t need = clis::ws_layout(B, H, Nq, Nk, d).total;
+  if (ws_bytes < need) return fail(CLIS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  return CLIS_OK;
+}
+
+clis::AttnArgs attn_args(const void* q, const void* k, const void* v, void* o, int B, int H, int Nq,
+                         int Nk, int d, float scale, int causal) {
+  clis::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.n_slots = B * H;
+  a.Nq = Nq; a.Nk = Nk; a.d = d;
+  a.c2 = (float)((double)scale * clis::kLog2e);
+  a.causal = causal ? 1 : 0;
+  return a;
+}
+
+hipError_t launch_attn(const clis::AttnArgs& a, int dtype, bool fixed, hipStream_t s) {
+  return dtype == CLIS_BF16 ? clis::launch_attn_bf16(a, fixed, s) : clis::launch_attn_fp32(a, fixed, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t clis_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 256;
+  return clis::ws_layout(B, H, Nq, Nk, d).total;
+}
+
+int clis_certify(const void* q, const void* k, const void* v, int B, int H, int Nq, int Nk, int d,
+                 float scale, int dtype, float* mu_out, int32_t* cert_out, clis_head_stats_t* stats_out,
+                 double* kbar_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  bool empty = false;
+  int st = check_common(B, H, Nq, Nk, d, scale, dtype, 0, &empty);
+  if (st != CLIS_OK || empty) return st;
+  if ((st = check_io(q, k, v, nullptr, false)) != CLIS_OK) return st;
+  if (!mu_out || !cert_out) return fail(CLIS_ERR_NULL, "mu_out and cert_out must be non-NULL");
+  if ((st = check_ws(ws, ws_bytes, B, H, Nq, Nk, d)) != CLIS_OK) return st;
+  return do_certify(q, k, v, B, H, Nq, Nk, d, scale, dtype, mu_out, cert_out, stats_out, kbar_out, ws,
+                    static_cast<hipStream_t>(stream));
+}
+
+int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int Nq, int Nk,
+                  int d, float scale, int causal, int dtype, int mode, const float* mu,
+                  const int32_t* cert, int32_t* route_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (mode != CLIS_MODE_AUTO && mode != CLIS_MODE_FIXED && mode != CLIS_MODE_ONLINE)
+    return fail(CLIS_ERR_UNSUPPORTED, "unknown mode %d", mode);
+  bool empty = false;
+  int st = check_common(B, H, Nq, Nk, d, scale, dtype, causal, &empty);
+  if (st != CLIS_OK || empty) return st;
+  if ((st = check_io(q, k, v, o, true)) != CLIS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  clis::AttnArgs a = attn_args(q, k, v, o, B, H, Nq, Nk, d, scale, causal);
+
+  if (mode == CLIS_MODE_ONLINE && !route_out) {
+    const hipError_t e = launch_attn(a, dtype, false, s);
+    return e == hipSuccess ? CLIS_OK : hip_fail(e, "online attention launch");
+  }
+  if ((st = check_ws(ws, ws_bytes, B, H, Nq, Nk, d)) != CLIS_OK) return st;
+  const clis::WsLayout L = clis::ws_layout(B, H, Nq, Nk, d);
+  const int BH = B * H;
+
+  const bool need_cert = (mode == CLIS_MODE_AUTO && (!cert || !mu)) || (mode == CLIS_MODE_FIXED && !mu);
+  const float* mu_use = mu;
+  const int32_t* cert_use = cert;
+  if (need_cert) {
+    float* mu_ws = at<float>(ws, L.mu);
+    int32_t* cert_ws = at<int32_t>(ws, L.cert);
+    st = do_certify(q, k, v, B, H, Nq, Nk, d, scale, dtype, mu_ws, cert_ws, nullptr, nullptr, ws, s);
+    if (st != CLIS_OK) return st;
+    mu_use = mu_ws;
+    cert_use = cert_ws;
+  }
+  int32_t* lists = at<int32_t>(ws, L.lists);
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  hipError_t e = clis::launch_route(cert_use, mode, BH, lists, counts, route_out, s);
+  if (e != hipSuccess) return hip_fail(e, "route launch");
+
+  // Each kernel's grid covers every head; slots past its list's count exit
+  // at once, so the routing needs no host round trip.
+  if (mode != CLIS_MODE_ONLINE) {
+    clis::AttnArgs f = a;
+    f.mu = mu_use;
+    f.head_list = lists;
+    f.head_count = counts;
+    if ((e = launch_attn(f, dtype, true, s)) != hipSuccess) return hip_fail(e, "fixed attention launch");
+  }
+  if (mode != CLIS_MODE_FIXED) {
+    clis::AttnArgs g = a;
+    g.head_list = lists + BH;
+    g.head_count = counts + 1;
+    if ((e = launch_attn(g, dtype, false, s)) != hipSuccess) return hip_fail(e, "online attention launch");
+  }
+  return CLIS_OK;
+}
+
+int online_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int Nq, int Nk,
+                    int d, float scale, int causal, int dtype, void* stream) {
+  return clis_attn_fwd(q, k, v, o, B, H, Nq, Nk, d, scale, causal, dtype, CLIS_MODE_ONLINE, nullptr,
+                       nullptr, nullptr, nullptr, 0, stream);
+}
+
+const char* clis_status_string(int status) {
+  switch (status) {
+    case CLIS_OK: return "ok";
+    case CLIS_ERR_NULL: return "null pointer";
+    case CLIS_ERR_SHAPE: return "invalid shape or scale";
+    case CLIS_ERR_UNSUPPORTED: return "unsupported head dim, dtype or mode";
+    case CLIS_ERR_ALIGN: return "misaligned pointer";
+    case CLIS_ERR_WORKSPACE: return "workspace missing or too small";
+    case CLIS_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* clis_last_error(void) { return g_err; }
+
+int clis_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,320 @@
+// certify.hip -- per-head certification pre-pass for CLiS attention on gfx950.
+//
+// Implements Algorithm 1 of "CLiS: Plug-and-Play Attention Acceleration for
+// Video Diffusion on TPUs via Certified Stabilization" (steps 1-7) plus the
+// fixed per-row stabilizer.  The pass is HBM-bound (it reads K twice and Q
+// and V once), so its arithmetic is fp64: cheap here, and it keeps the flag
+// decision B_h <= C in the same precision as an fp64 reference.
+//
+// Kernels, in stream order:
+//   1. cert_keys_values: per (head, key split) partial column sums of K and
+//      partial max |V|                                   (steps 1 and 5)
+//   2. cert_kbar: kbar = (sum of partials in split order) / Nk      (step 1)
+//   3. cert_norms: key splits -> partial max ||k - kbar||^2 (steps 2-3);
+//      query splits -> partial max ||q||^2 and mu_r = c (q_r . kbar)
+//   4. cert_finalize: kappa, B_h, G, A, C, flag per head         (steps 3-7)
+// Every reduction has a fixed order (no atomics), so results are bitwise
+// reproducible.  Maxima propagate NaN so that a NaN input never certifies.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "internal.h"
+
+namespace clis {
+namespace {
+
+constexpr int kThreads = 256;
+
+// max that keeps NaN once seen (fmax would drop it).
+__device__ __forceinline__ double max_keep_nan(double acc, double x) {
+  return (x > acc || x != x) ? x : acc;
+}
+
+// Elements per 16-byte vector load.
+template <typename T> struct Vec;
+template <> struct Vec<uint16_t> { static constexpr int n = 8; };
+template <> struct Vec<float> { static constexpr int n = 4; };
+
+__device__ __forceinline__ double to_f64(uint16_t b) {
+  return (double)__uint_as_float((uint32_t)b << 16);
+}
+__device__ __forceinline__ double to_f64(float f) { return (double)f; }
+
+// 16 bytes of row elements, widened to fp64.
+template <typename T>
+__device__ __forceinline__ void load_vec(const T* p, double* out) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = (double)__uint_as_float(w[i] << 16);
+      out[2 * i + 1] = (double)__uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    out[0] = (double)__uint_as_float(u.x);
+    out[1] = (double)__uint_as_float(u.y);
+    out[2] = (double)__uint_as_float(u.z);
+    out[3] = (double)__uint_as_float(u.w);
+  }
+}
+
+__device__ __forceinline__ void split_range(int n, int splits, int s, int* lo, int* hi) {
+  const long long per = ((long long)n + splits - 1) / splits;
+  long long a = per * s, b = a + per;
+  if (a > n) a = n;
+  if (b > n) b = n;
+  *lo = (int)a;
+  *hi = (int)b;
+}
+
+// Block-wide NaN-keeping max; every thread gets the result.
+__device__ double block_max(double x, double* red) {
+  for (int off = 32; off > 0; off >>= 1) x = max_keep_nan(x, __shfl_xor(x, off));
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  double r = red[0];
+  for (int i = 1; i < kThreads / 64; ++i) r = max_keep_nan(r, red[i]);
+  return r;
+}
+
+// Step 1 (partial column sums of K) and step 5 (partial max |V|).
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads)
+cert_keys_values(const T* __restrict__ K, const T* __restrict__ V, int Nk, int Sk,
+                 double* __restrict__ ksum_part, double* __restrict__ vmax_part) {
+  constexpr int VEC = Vec<T>::n, TPR = D / VEC, RPI = kThreads / TPR;
+  __shared__ double colsum[RPI][D];
+  __shared__ double red[kThreads / 64];
+  const int bh = blockIdx.y, split = blockIdx.x;
+  int lo, hi;
+  split_range(Nk, Sk, split, &lo, &hi);
+  const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
+  const T* kb = K + (size_t)bh * Nk * D;
+  const T* vb = V + (size_t)bh * Nk * D;
+  double acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+  double vmax = 0.0;
+  for (int j = lo + tr; j < hi; j += RPI) {
+    double x[VEC];
+    load_vec(kb + (size_t)j * D + tc * VEC, x);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += x[e];
+    load_vec(vb + (size_t)j * D + tc * VEC, x);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) vmax = max_keep_nan(vmax, fabs(x[e]));
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) colsum[tr][tc * VEC + e] = acc[e];
+  vmax = block_max(vmax, red);  // contains __syncthreads
+  double* out = ksum_part + ((size_t)bh * Sk + split) * D;
+  for (int c = threadIdx.x; c < D; c += kThreads) {
+    double s = 0.0;
+    for (int r = 0; r < RPI; ++r) s += colsum[r][c];  // fixed row-group order
+    out[c] = s;
+  }
+  if (threadIdx.x == 0) vmax_part[(size_t)bh * Sk + split] = vmax;
+}
+
+// Step 1: kbar from the split partials, summed in split order.
+template <int D>
+__global__ void __launch_bounds__(D)
+cert_kbar(const double* __restrict__ ksum_part, int Nk, int Sk, double* __restrict__ kbar) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  const double* p = ksum_part + (size_t)bh * Sk * D + c;
+  double s = 0.0;
+  for (int i = 0; i < Sk; ++i) s += p[(size_t)i * D];
+  kbar[(size_t)bh * D + c] = s / (double)Nk;
+}
+
+// Sum over the TPR consecutive lanes that hold one row, in a fixed xor order.
+template <int TPR>
+__device__ __forceinline__ double row_sum(double x) {
+#pragma unroll
+  for (int off = 1; off < TPR; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// Steps 2-3 on key splits; ||q||^2 and the stabilizers on query splits.
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads)
+cert_norms(const T* __restrict__ Q, const T* __restrict__ K, const double* __restrict__ kbar,
+           int Nq, int Nk, int Sk, int Sq, double c2, float* __restrict__ mu,
+           double* __restrict__ kap_part, double* __restrict__ qss_part) {
+  constexpr int VEC = Vec<T>::n, TPR = D / VEC, RPI = kThreads / TPR;
+  __shared__ double red[kThreads / 64];
+  const int bh = blockIdx.y;
+  const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
+  double kb[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) kb[e] = kbar[(size_t)bh * D + tc * VEC + e];
+  double best = 0.0;
+  if ((int)blockIdx.x < Sk) {
+    const int split = blockIdx.x;
+    int lo, hi;
+    split_range(Nk, Sk, split, &lo, &hi);
+    const T* base = K + (size_t)bh * Nk * D;
+    // every lane of a row group runs the same trip count, so the shuffles
+    // inside row_sum always see their partners
+    for (int j0 = lo; j0 < hi; j0 += RPI) {
+      const int j = j0 + tr;
+      double ss = 0.0;
+      if (j < hi) {
+        double x[VEC];
+        load_vec(base + (size_t)j * D + tc * VEC, x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const double t = x[e] - kb[e];
+          ss += t * t;
+        }
+      }
+      ss = row_sum<TPR>(ss);
+      if (j < hi) best = max_keep_nan(best, ss);
+    }
+    best = block_max(best, red);
+    if (threadIdx.x == 0) kap_part[(size_t)bh * Sk + split] = best;
+  } else {
+    const int split = blockIdx.x - Sk;
+    int lo, hi;
+    split_range(Nq, Sq, split, &lo, &hi);
+    const T* base = Q + (size_t)bh * Nq * D;
+    for (int r0 = lo; r0 < hi; r0 += RPI) {
+      const int r = r0 + tr;
+      double ss = 0.0, dot = 0.0;
+      if (r < hi) {
+        double x[VEC];
+        load_vec(base + (size_t)r * D + tc * VEC, x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          ss += x[e] * x[e];
+          dot += x[e] * kb[e];
+        }
+      }
+      ss = row_sum<TPR>(ss);
+      dot = row_sum<TPR>(dot);
+      if (r < hi) {
+        best = max_keep_nan(best, ss);
+        if (tc == 0) mu[(size_t)bh * Nq + r] = (float)(c2 * dot);
+      }
+    }
+    best = block_max(best, red);
+    if (threadIdx.x == 0) qss_part[(size_t)bh * Sq + split] = best;
+  }
+}
+
+// ceil(log2 x) for finite x >= 1, exactly.
+__device__ __forceinline__ int ceil_log2_f64(double x) {
+  int e;
+  const double f = frexp(x, &e);
+  return (f == 0.5) ? e - 1 : e;
+}
+
+// Steps 3-7 and the flag, one thread per head.
+__global__ void __launch_bounds__(kThreads)
+cert_finalize(const double* __restrict__ vmax_part, const double* __restrict__ kap_part,
+              const double* __restrict__ qss_part, int BH, int Nk, int Sk, int Sq, double c2,
+              int32_t* __restrict__ cert, clis_head_stats_t* __restrict__ stats) {
+  for (int h = blockIdx.x * kThreads + threadIdx.x; h < BH; h += gridDim.x * kThreads) {
+    double vmax = 0.0, kap2 = 0.0, qss = 0.0;
+    for (int i = 0; i < Sk; ++i) {
+      vmax = max_keep_nan(vmax, vmax_part[(size_t)h * Sk + i]);
+      kap2 = max_keep_nan(kap2, kap_part[(size_t)h * Sk + i]);
+    }
+    for (int i = 0; i < Sq; ++i) qss = max_keep_nan(qss, qss_part[(size_t)h * Sq + i]);
+    const double kappa = sqrt(kap2);
+    const double qmax = sqrt(qss);
+    const double bound = (c2 * qmax) * kappa;
+    // step 5; a non-finite max |V| gets G = 128 so that C < 0
+    const int G = isfinite(vmax) ? ceil_log2_f64(vmax > 1.0 ? vmax : 1.0) : 128;
+    // step 6: ceil(log2 Nk) for Nk >= 1
+    const int L = (Nk <= 1) ? 0 : 32 - __clz(Nk - 1);
+    const int A = L + G;
+    // step 7 with the Figure 3 limits of fp32 accumulators and bf16/fp32 exp2
+    // outputs: log2 of the largest finite value is 127.99... in both formats,
+    // so floor(U_exp) = 127 and ceil(U_acc - A) - 1 = 127 - A for integer A.
+    const int C = min(127, 127 - A);
+    const int ok = (isfinite(bound) && bound <= (double)C) ? 1 : 0;
+    cert[h] = ok;
+    clis_head_stats_t st;
+    st.kappa = kappa;
+    st.qnorm_max = qmax;
+    st.bound = bound;
+    st.maxabs_v = vmax;
+    st.G = G;
+    st.L = L;
+    st.A = A;
+    st.C = C;
+    st.cert = ok;
+    st.reserved = 0;
+    stats[h] = st;
+  }
+}
+
+__global__ void __launch_bounds__(64)
+route_heads(const int32_t* __restrict__ cert, int mode, int BH, int32_t* __restrict__ lists,
+            int32_t* __restrict__ counts, int32_t* __restrict__ route_out) {
+  // One wave compacts the heads in index order: ballot + prefix popcount.
+  const int lane = threadIdx.x;
+  int nf = 0, no = 0;
+  for (int base = 0; base < BH; base += 64) {
+    const int h = base + lane;
+    int fixed = 0;
+    if (h < BH) fixed = (mode == CLIS_MODE_FIXED) || (mode == CLIS_MODE_AUTO && cert[h] != 0);
+    const unsigned long long fm = __ballot(h < BH && fixed);
+    const unsigned long long om = __ballot(h < BH && !fixed);
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (h < BH) {
+      if (fixed) lists[nf + __popcll(fm & below)] = h;
+      else lists[BH + no + __popcll(om & below)] = h;
+      if (route_out) route_out[h] = fixed;
+    }
+    nf += __popcll(fm);
+    no += __popcll(om);
+  }
+  if (lane == 0) {
+    counts[0] = nf;
+    counts[1] = no;
+  }
+}
+
+template <typename T, int D>
+hipError_t certify_typed(const CertifyArgs& a, hipStream_t s) {
+  const int BH = a.B * a.H;
+  const int Sk = cert_splits(a.Nk), Sq = cert_splits(a.Nq);
+  const double c2 = (double)a.scale * kLog2e;
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  cert_keys_values<T, D><<<dim3(Sk, BH), kThreads, 0, s>>>(k, v, a.Nk, Sk, a.ksum_part, a.vmax_part);
+  cert_kbar<D><<<BH, D, 0, s>>>(a.ksum_part, a.Nk, Sk, a.kbar);
+  cert_norms<T, D><<<dim3(Sk + Sq, BH), kThreads, 0, s>>>(q, k, a.kbar, a.Nq, a.Nk, Sk, Sq, c2, a.mu,
+                                                          a.kap_part, a.qss_part);
+  const int fb = (BH + kThreads - 1) / kThreads;
+  cert_finalize<<<fb, kThreads, 0, s>>>(a.vmax_part, a.kap_part, a.qss_part, BH, a.Nk, Sk, Sq, c2,
+                                        a.cert, a.stats);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_certify(const CertifyArgs& a, hipStream_t s) {
+  if (a.dtype == CLIS_BF16) {
+    if (a.d == 128) return certify_typed<uint16_t, 128>(a, s);
+    if (a.d == 64) return certify_typed<uint16_t, 64>(a, s);
+  } else {
+    if (a.d == 128) return certify_typed<float, 128>(a, s);
+    if (a.d == 64) return certify_typed<float, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_route(const int32_t* cert, int mode, int BH, int32_t* lists, int32_t* counts,
+                        int32_t* route_out, hipStream_t s) {
+  route_heads<<<1, 64, 0, s>>>(cert, mode, BH, lists, counts, route_out);
+  return hipGetLastError();
+}
+
+}  // namespace clis

@@ -1,0 +1,92 @@
+// internal.h -- kernel launchers and workspace layout shared by the library's
+// translation units (not part of the public ABI; see include/clis.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "clis.h"
+
+namespace clis {
+
+// log2(e) in fp64; the exp2 arguments of the kernels are c = scale * log2(e)
+// times a dot product, so that exp2 (the gfx950 v_exp_f32) replaces exp.
+constexpr double kLog2e = 1.442695040888963407359924681001892137;
+
+// Rows of one head handled by one certification block: heads are split so
+// that a launch has enough blocks to cover the chip (the split counts are a
+// pure function of the shape, so the workspace size is too).
+inline int cert_splits(int n) {
+  int s = (n + 1023) / 1024;
+  return s < 1 ? 1 : (s > 64 ? 64 : s);
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Byte offsets of every region inside the caller's workspace.
+struct WsLayout {
+  size_t ksum_part;  // [BH][Sk][d] fp64   partial key column sums
+  size_t vmax_part;  // [BH][Sk]    fp64   partial max |V|
+  size_t kap_part;   // [BH][Sk]    fp64   partial max ||k - kbar||^2
+  size_t qss_part;   // [BH][Sq]    fp64   partial max ||q||^2
+  size_t kbar;       // [BH][d]     fp64
+  size_t stats;      // [BH]        clis_head_stats_t
+  size_t mu;         // [BH][Nq]    fp32   stabilizers when the caller gave none
+  size_t cert;       // [BH]        int32
+  size_t lists;      // [2][BH]     int32  heads routed fixed / online
+  size_t counts;     // [2]         int32
+  size_t total;
+};
+
+inline WsLayout ws_layout(int B, int H, int Nq, int Nk, int d) {
+  const size_t BH = (size_t)B * H, Sk = cert_splits(Nk), Sq = cert_splits(Nq);
+  WsLayout w{};
+  size_t o = 0;
+  w.ksum_part = o; o = align256(o + BH * Sk * d * sizeof(double));
+  w.vmax_part = o; o = align256(o + BH * Sk * sizeof(double));
+  w.kap_part = o;  o = align256(o + BH * Sk * sizeof(double));
+  w.qss_part = o;  o = align256(o + BH * Sq * sizeof(double));
+  w.kbar = o;      o = align256(o + BH * d * sizeof(double));
+  w.stats = o;     o = align256(o + BH * sizeof(clis_head_stats_t));
+  w.mu = o;        o = align256(o + BH * (size_t)Nq * sizeof(float));
+  w.cert = o;      o = align256(o + BH * sizeof(int32_t));
+  w.lists = o;     o = align256(o + 2 * BH * sizeof(int32_t));
+  w.counts = o;    o = align256(o + 2 * sizeof(int32_t));
+  w.total = o;
+  return w;
+}
+
+struct CertifyArgs {
+  const void* q; const void* k; const void* v;
+  int B, H, Nq, Nk, d;
+  float scale;
+  int dtype;
+  float* mu;                 // [BH][Nq]
+  int32_t* cert;             // [BH]
+  clis_head_stats_t* stats;  // [BH] (never NULL here: workspace copy if the caller gave none)
+  double* kbar;              // [BH][d]
+  double* ksum_part; double* vmax_part; double* kap_part; double* qss_part;
+};
+
+hipError_t launch_certify(const CertifyArgs& a, hipStream_t s);
+
+// Builds the fixed / online head lists from cert and mode (one tiny kernel).
+hipError_t launch_route(const int32_t* cert, int mode, int BH, int32_t* lists, int32_t* counts,
+                        int32_t* route_out, hipStream_t s);
+
+struct AttnArgs {
+  const void* q; const void* k; const void* v; void* o;
+  const float* mu;            // fixed path only
+  const int32_t* head_list;   // NULL: every head, in order
+  const int32_t* head_count;  // device count of head_list entries
+  int n_slots;                // heads the grid covers (B*H)
+  int Nq, Nk, d;
+  float c2;                   // scale * log2(e), rounded to fp32
+  int causal;
+};
+
+hipError_t launch_attn_bf16(const AttnArgs& a, bool fixed, hipStream_t s);
+hipError_t launch_attn_fp32(const AttnArgs& a, bool fixed, hipStream_t s);
+
+}  // namespace clis

@@ -1,0 +1,115 @@
+"""The C-ABI library loads and exports every symbol include/clis.h declares,
+and its argument checks reject bad calls before touching the GPU (CPU only:
+no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "clis.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+@pytest.fixture(scope="module")
+def clis():
+    import softmax_stabilization_video_amd as m
+    return m
+
+
+def test_header_declares_the_three_entry_points():
+    names = _declared_functions()
+    for n in ("clis_certify", "clis_attn_fwd", "online_attn_fwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(clis):
+    raw = ctypes.CDLL(clis.LIB_PATH)
+    names = _declared_functions()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(raw, n), f"libclis.so does not export {n}"
+    assert sorted(names) == sorted(clis.EXPORTS)
+
+
+def test_abi_version_and_strings(clis):
+    assert clis.lib.clis_abi_version() == 1
+    assert clis.lib.clis_status_string(0) == b"ok"
+    assert clis.lib.clis_status_string(5).startswith(b"workspace")
+    assert clis.lib.clis_status_string(99) == b"unknown status"
+
+
+def test_stats_struct_size_matches_header(clis):
+    assert clis.STATS_BYTES == 56
+
+
+def test_workspace_size_is_monotone(clis):
+    a = clis.workspace_bytes(1, 20, 75600, 75600, 128)
+    b = clis.workspace_bytes(1, 20, 1000, 1000, 128)
+    assert a > b > 0 and a % 256 == 0
+    assert clis.workspace_bytes(0, 1, 1, 1, 64) == 256
+
+
+def _fake(addr=0x10000):
+    return ctypes.c_void_p(addr)
+
+
+@pytest.mark.parametrize("case,expected", [
+    (dict(d=96), 3),                     # unsupported head dim
+    (dict(dtype=7), 3),                  # unknown dtype
+    (dict(mode=9), 3),                   # unknown mode
+    (dict(Nq=10, Nk=12, causal=1), 2),   # causal needs Nq == Nk
+    (dict(scale=0.0), 2),
+    (dict(scale=float("inf")), 2),
+    (dict(B=-1), 2),
+    (dict(Nk=0), 2),                     # query rows but no keys
+    (dict(q=None), 1),
+    (dict(o=None), 1),
+    (dict(q=0x10008), 4),                # not 16-byte aligned
+    (dict(ws=None, mode=0), 5),          # auto mode needs a workspace
+    (dict(ws_bytes=10, mode=0), 5),
+])
+def test_argument_checks_reject_before_launch(clis, case, expected):
+    a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, B=1, H=2, Nq=10, Nk=10, d=64, scale=0.125,
+             causal=0, dtype=0, mode=1, ws=0x50000, ws_bytes=1 << 30)
+    a.update(case)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = clis.lib.clis_attn_fwd(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), a["B"], a["H"], a["Nq"],
+                                a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], a["mode"], None, None,
+                                None, vp(a["ws"]), a["ws_bytes"], None)
+    assert st == expected, clis.lib.clis_last_error()
+    assert clis.lib.clis_last_error() != b""
+
+
+def test_empty_batch_is_a_no_op(clis):
+    # nothing to compute: CLIS_OK without touching any pointer
+    for B, H, Nq in ((0, 4, 10), (2, 0, 10), (2, 4, 0)):
+        assert clis.lib.clis_attn_fwd(None, None, None, None, B, H, Nq, 10, 128, 0.1, 0, 0, 0, None, None,
+                                      None, None, 0, None) == 0
+        assert clis.lib.online_attn_fwd(None, None, None, None, B, H, Nq, 10, 128, 0.1, 0, 0, None) == 0
+        assert clis.lib.clis_certify(None, None, None, B, H, Nq, 10, 128, 0.1, 0, None, None, None, None,
+                                     None, 0, None) == 0
+
+
+def test_certify_requires_outputs(clis):
+    st = clis.lib.clis_certify(_fake(), _fake(), _fake(), 1, 1, 8, 8, 64, 0.1, 0, None, None, None, None,
+                               _fake(0x1000000), 1 << 30, None)
+    assert st == 1
+
+
+def test_product_path_never_touches_the_oracle():
+    """The HIP library's sources and binding name nothing under oracle/."""
+    pkg = os.path.join(ROOT, "softmax_stabilization_video_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
+                assert "oracle.c" not in text and "_oracle.so" not in text, f

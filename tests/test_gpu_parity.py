@@ -1,0 +1,292 @@
+"""GPU parity: the HIP library, called through its C ABI, against the fp64
+oracle on the same seeded inputs.
+
+Certification: flags bit-exact, the integers G, L, A, C exact, max|V| exact,
+kappa / B_h / kbar to fp64 rounding, mu to fp32 rounding.  The flag is a
+decision B_h <= C taken in fp64 on both sides; each case first asserts that
+the oracle's B_h is not within 1e-9 (relative) of C, where the two fp64
+summation orders could disagree.
+Attention: bf16 within max abs 2e-2, mean abs 1e-3 and rel L2 5e-3 of the
+oracle; fp32 within max abs 1e-5.  Routing: auto mode's output for every
+head is bitwise equal to the forced mode of the route it took.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_util import assert_close, assert_valid, errors, say, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def clis():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import softmax_stabilization_video_amd as m
+    return m
+
+
+def _inputs(w, seed=0):
+    Q, K, V = workloads.make_inputs(w, seed)
+    return (Q, K, V), tuple(to_device(a, w.dtype) for a in (Q, K, V))
+
+
+def check_certify(clis, w, host, dev, margin=1e-9):
+    """Run clis_certify on the device and compare with the oracle per head."""
+    import torch
+    say("certify", w.name, w.B, w.H, w.Nq, w.Nk, w.d, w.dtype)
+    mu, cert, stats, kbar = clis.clis_certify(*dev, w.scale, want_stats=True)
+    torch.cuda.synchronize()
+    ref = oracle.certify(*host, w.dtype, w.scale)
+    fin = np.isfinite(ref["bound"])
+    gap = np.abs(ref["bound"] - ref["C"])
+    assert np.all(~fin | (gap > margin * np.maximum(1.0, np.abs(ref["C"])))), "case too close to the cap"
+    st = clis.decode_stats(stats).reshape(w.B, w.H)
+    assert np.array_equal(cert.cpu().numpy(), ref["cert"]), (cert.cpu().numpy(), ref["cert"])
+    assert np.array_equal(st["cert"], ref["cert"])
+    for n in ("G", "L", "A", "C"):
+        assert np.array_equal(st[n], ref[n]), n
+    assert np.array_equal(st["maxabs_v"], ref["maxabs_v"])
+    np.testing.assert_allclose(st["kappa"], ref["kappa"], rtol=1e-12)
+    np.testing.assert_allclose(st["qnorm_max"], ref["qnorm_max"], rtol=1e-12)
+    np.testing.assert_allclose(st["bound"], ref["bound"], rtol=1e-12)
+    np.testing.assert_allclose(kbar.cpu().numpy(), ref["kbar"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(mu.cpu().numpy(), ref["mu"], rtol=2e-7, atol=1e-7)
+    return mu, cert, ref
+
+
+def run_attention(clis, w, host, dev, mu, cert, rows=None, modes=("fixed", "online", "auto")):
+    """Every mode on the device, compared with the oracle (all rows or `rows`)."""
+    import torch
+    want = oracle.attention(*host, w.dtype, w.scale, w.causal, rows=rows)
+    outs = {}
+    for m in modes:
+        say("attn", m, w.name, w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, "causal" if w.causal else "dense")
+        o, route = clis.clis_attn_fwd(*dev, w.scale, w.causal, mode=m, want_route=True)
+        torch.cuda.synchronize()
+        outs[m] = o
+        r = route.cpu().numpy()
+        if m == "fixed":
+            assert np.all(r == 1)
+        elif m == "online":
+            assert np.all(r == 0)
+        else:
+            assert np.array_equal(r, cert.cpu().numpy())
+    c = cert.cpu().numpy().astype(bool)
+    errs = {}
+    ridx = None if rows is None else torch.as_tensor(rows, device=dev[0].device)
+    for m, o in outs.items():
+        got = to_f64(o if ridx is None else o.index_select(2, ridx))
+        # forced-fixed output is only promised on certified heads
+        sel = c if m == "fixed" else np.ones_like(c)
+        if sel.any():
+            errs[m] = assert_close(got[sel], want[sel], w.dtype, f"{w.name}/{m}")
+    if "auto" in outs and "fixed" in outs and "online" in outs:
+        for b in range(w.B):
+            for h in range(w.H):
+                ref = outs["fixed"] if c[b, h] else outs["online"]
+                assert torch.equal(outs["auto"][b, h], ref[b, h]), (b, h)
+    return outs, errs
+
+
+# ---------------------------------------------------------------- small cases
+def test_tiny_fp32_workload_all_rows(clis):
+    w = workloads.WORKLOADS["tiny"]
+    host, dev = _inputs(w)
+    mu, cert, ref = check_certify(clis, w, host, dev)
+    assert ref["cert"].all()
+    _, errs = run_attention(clis, w, host, dev, mu, cert)
+    assert errs["fixed"]["max_abs"] <= 1e-5 and errs["online"]["max_abs"] <= 1e-5
+
+
+SMALL = [
+    # name, B, H, Nq, Nk, d, dtype, causal
+    ("bf16_tail_d128", 1, 2, 1000, 1000, 128, "bf16", False),
+    ("bf16_tail_d64", 1, 2, 1000, 1000, 64, "bf16", False),
+    ("bf16_exact_tiles", 1, 1, 256, 256, 128, "bf16", False),
+    ("bf16_causal_tail", 1, 3, 777, 777, 128, "bf16", True),
+    ("bf16_causal_d64", 2, 1, 300, 300, 64, "bf16", True),
+    ("bf16_cross", 2, 1, 300, 1300, 128, "bf16", False),
+    ("bf16_lt_tile", 1, 1, 5, 5, 128, "bf16", False),
+    ("bf16_one_key", 1, 2, 70, 1, 128, "bf16", False),
+    ("bf16_one_query", 1, 2, 1, 333, 128, "bf16", False),
+    ("fp32_tail_d64", 1, 2, 1000, 1000, 64, "fp32", False),
+    ("fp32_tail_d128", 1, 2, 1000, 1000, 128, "fp32", False),
+    ("fp32_causal", 1, 2, 700, 700, 128, "fp32", True),
+    ("fp32_cross", 1, 2, 33, 517, 64, "fp32", False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_shapes_all_rows(clis, case):
+    name, B, H, Nq, Nk, d, dtype, causal = case
+    w = workloads.custom(name, B, H, Nq, d, dtype, causal, key_bias_std=2.0, Nk=Nk)
+    host, dev = _inputs(w, seed=11)
+    mu, cert, ref = check_certify(clis, w, host, dev)
+    assert ref["cert"].all()
+    run_attention(clis, w, host, dev, mu, cert)
+
+
+def test_mixed_routing_small(clis):
+    """A quarter of the heads scaled past the cap: flags, routes and per-head
+    outputs (auto equals the forced route bitwise)."""
+    w = workloads.custom("mixed_small", 2, 8, 1500, 128, "bf16", False, base="mixed")
+    host, dev = _inputs(w, seed=3)
+    mu, cert, ref = check_certify(clis, w, host, dev)
+    fails = set(workloads.failing_heads(w, 3).tolist())
+    assert len(fails) == 4
+    assert {i for i, c in enumerate(ref["cert"].ravel()) if not c} == fails
+    run_attention(clis, w, host, dev, mu, cert)
+
+
+def test_caller_supplied_certificate_is_used(clis):
+    """mu/cert passed in: same result as letting the call certify itself."""
+    import torch
+    w = workloads.custom("given_cert", 1, 4, 600, 128, "bf16", False, base="mixed")
+    _, dev = _inputs(w, seed=5)
+    mu, cert = clis.clis_certify(*dev, w.scale)
+    a = clis.clis_attn_fwd(*dev, w.scale, mode="auto", mu=mu, cert=cert)
+    b = clis.clis_attn_fwd(*dev, w.scale, mode="auto")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    # flipping the flags the caller passes flips the routes
+    flipped = 1 - cert
+    c, route = clis.clis_attn_fwd(*dev, w.scale, mode="auto", mu=mu, cert=flipped, want_route=True)
+    torch.cuda.synchronize()
+    assert torch.equal(route, flipped)
+
+
+def test_online_entry_point_equals_online_mode(clis):
+    import torch
+    for causal in (False, True):
+        w = workloads.custom("online_eq", 1, 3, 500, 128, "bf16", causal)
+        _, dev = _inputs(w, seed=7)
+        a = clis.online_attn_fwd(*dev, w.scale, causal)
+        b = clis.clis_attn_fwd(*dev, w.scale, causal, mode="online")
+        c = clis.clis_attn_fwd(*dev, w.scale, causal, mode="online", want_route=True)[0]
+        torch.cuda.synchronize()
+        assert torch.equal(a, b) and torch.equal(a, c)
+
+
+def test_bitwise_reproducible(clis):
+    import torch
+    w = workloads.custom("repro", 1, 2, 900, 128, "bf16", False)
+    _, dev = _inputs(w, seed=8)
+    runs = [clis.clis_attn_fwd(*dev, w.scale, mode="auto") for _ in range(3)]
+    cs = [clis.clis_certify(*dev, w.scale) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(runs[0], r) for r in runs[1:])
+    assert torch.equal(cs[0][0], cs[1][0]) and torch.equal(cs[0][1], cs[1][1])
+
+
+def test_non_finite_input_never_certifies(clis):
+    """A NaN key makes its head uncertified; the online fallback propagates
+    NaN like standard attention, and other heads are untouched."""
+    import torch
+    w = workloads.custom("nan", 1, 3, 200, 128, "bf16", False)
+    (Q, K, V), _ = _inputs(w, seed=9)
+    K = K.copy()
+    K[0, 1, 17, 5] = 0x7FC0  # bf16 quiet NaN
+    dev = tuple(to_device(a, w.dtype) for a in (Q, K, V))
+    mu, cert = clis.clis_certify(*dev, w.scale)
+    o = clis.clis_attn_fwd(*dev, w.scale, mode="auto")
+    torch.cuda.synchronize()
+    assert cert.cpu().numpy().tolist() == [[1, 0, 1]]
+    got = to_f64(o)
+    assert np.all(np.isnan(got[0, 1]))
+    want = oracle.attention(Q, K, V, w.dtype, w.scale)
+    assert np.all(np.isnan(want[0, 1]))
+    for h in (0, 2):
+        assert_close(got[0, h], want[0, h], "bf16", f"nan/head{h}")
+
+
+def test_certified_head_near_the_cap_stays_finite(clis):
+    """A head whose bound sits just under C, with one query aligned to one
+    outlying key so the largest exp2 argument nearly reaches the bound."""
+    import torch
+    d, n = 128, 700
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((n, d)).astype(np.float32)
+    k = rng.standard_normal((n, d)).astype(np.float32)
+    v = rng.standard_normal((n, d)).astype(np.float32)
+    k[3] = 0.0
+    k[3, 0] = 40.0
+    scale = float(np.float32(1 / math.sqrt(d)))  # the fp32 value the library receives
+    host0 = tuple(workloads.round_to_bf16_bits(a)[None, None] for a in (q, k, v))
+    base = oracle.certify(*host0, "bf16", scale)
+    # put q row 0 along e1 with the largest norm, sized so B_h ~ (1 - 1e-2) C
+    # (bf16 rounding of that row moves the bound by < 0.4%)
+    c2 = scale * math.log2(math.e)
+    target = (1 - 1e-2) * base["C"][0, 0] / (c2 * base["kappa"][0, 0])
+    q[0] = 0.0
+    q[0, 0] = target
+    host = tuple(workloads.round_to_bf16_bits(a)[None, None] for a in (q, k, v))
+    dev = tuple(to_device(a, "bf16") for a in host)
+    w = workloads.custom("near_cap", 1, 1, n, d, "bf16", False)
+    mu, cert, ref = check_certify(clis, w, host, dev)
+    assert ref["cert"][0, 0] == 1 and ref["bound"][0, 0] > 0.98 * ref["C"][0, 0]
+    qd = oracle.decode(host[0][0, 0], "bf16")
+    kd = oracle.decode(host[1][0, 0], "bf16")
+    _, mx, _ = oracle.fixed_mu_head(qd, kd, oracle.decode(host[2][0, 0], "bf16"), scale, ref["mu"][0, 0],
+                                    rows=np.array([0]))
+    assert mx[0] > 0.9 * ref["C"][0, 0]
+    o = clis.clis_attn_fwd(*dev, scale, mode="fixed", mu=mu)
+    torch.cuda.synchronize()
+    want = oracle.attention(*host, "bf16", scale)
+    got = to_f64(o)
+    assert_valid(got, "near_cap")
+    assert_close(got, want, "bf16", "near_cap")
+
+
+def test_forced_fixed_on_failing_head_is_invalid(clis):
+    """Why certification exists: the fixed stabilizer on a head far past the
+    cap overflows (NaN/Inf), while auto mode routes it online and is valid."""
+    import torch
+    w = workloads.custom("force_fail", 1, 1, 512, 128, "bf16", False, fail_frac=1.0, fail_qk_scale=40.0,
+                         outlier_frac=0.01, outlier_scale=200.0)
+    host, dev = _inputs(w, seed=4)
+    mu, cert = clis.clis_certify(*dev, w.scale)
+    o_fixed = clis.clis_attn_fwd(*dev, w.scale, mode="fixed", mu=mu)
+    o_auto = clis.clis_attn_fwd(*dev, w.scale, mode="auto")
+    torch.cuda.synchronize()
+    assert cert.item() == 0
+    assert not np.all(np.isfinite(to_f64(o_fixed)))
+    assert_valid(to_f64(o_auto), "force_fail/auto")
+
+
+def test_empty_and_errors_through_binding(clis):
+    import torch
+    q = torch.zeros((0, 2, 10, 128), dtype=torch.bfloat16, device="cuda")
+    o = clis.clis_attn_fwd(q, q, q)
+    assert o.shape == q.shape
+    x = torch.zeros((1, 1, 16, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(clis.ClisError) as e:
+        clis.clis_attn_fwd(x, x, x)
+    assert e.value.status == 3
+
+
+# ---------------------------------------------------------------- full sizes
+FULL = ["wan720p", "wan480p", "mixed", "causal"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(clis, name):
+    """Full-size inputs: certification on every head, attention on sampled
+    rows (ends, tile edges, seeded rows) in every mode."""
+    w = workloads.WORKLOADS[name]
+    say("generate", name)
+    host, dev = _inputs(w, seed=0)
+    mu, cert, ref = check_certify(clis, w, host, dev)
+    fails = set(workloads.failing_heads(w, 0).tolist())
+    assert {i for i, c in enumerate(ref["cert"].ravel()) if not c} == fails
+    rows = workloads.sample_rows(w, n_random=16, tiles=(128,))
+    outs, errs = run_attention(clis, w, host, dev, mu, cert, rows=rows)
+    say("errors", name, errs)
+    import torch
+    auto = outs["auto"]
+    assert bool(torch.isfinite(auto).all()) and bool((auto != 0).any()), f"{name}: invalid output"

@@ -47,16 +47,26 @@ class Workload:
     outlier_frac: float = 0.0   # fraction of key rows scaled further on those heads
     outlier_scale: float = 1.0
     note: str = ""
+    Nk_: int | None = None      # key/value rows when they differ from the query rows
+
+    @property
+    def Nq(self) -> int:
+        return self.N
+
+    @property
+    def Nk(self) -> int:
+        return self.N if self.Nk_ is None else self.Nk_
 
     @property
     def scale(self) -> float:
-        return 1.0 / math.sqrt(self.d)
+        """1/sqrt(d) as the fp32 value the library receives (its ABI takes fp32)."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
 
     def flops(self) -> float:
         """Attention FLOPs of one forward call: 4*d per unmasked score."""
         if self.causal:
             return 4.0 * self.B * self.H * self.d * self.N * (self.N + 1) / 2
-        return 4.0 * self.B * self.H * self.N * self.N * self.d
+        return 4.0 * self.B * self.H * self.Nq * self.Nk * self.d
 
 
 def latent_tokens(frames: int, height: int, width: int) -> int:
@@ -80,15 +90,16 @@ WORKLOADS = {
 
 
 def custom(name: str, B: int, H: int, N: int, d: int, dtype: str = "bf16", causal: bool = False,
-           key_bias_std: float = 2.0, base: str | None = None, **kw) -> Workload:
-    """A workload of the given shape with another workload's distribution."""
+           key_bias_std: float = 2.0, base: str | None = None, Nk: int | None = None, **kw) -> Workload:
+    """A workload of the given shape (Nk: key rows, default N) with another
+    workload's distribution, or plain Gaussians plus a key bias."""
     if base is not None:
         w = WORKLOADS[base]
         params = dict(key_bias_std=w.key_bias_std, fail_frac=w.fail_frac, fail_qk_scale=w.fail_qk_scale,
                       outlier_frac=w.outlier_frac, outlier_scale=w.outlier_scale)
         params.update(kw)
-        return Workload(name, 100 + w.cfg_id, B, H, N, d, dtype, causal, **params)
-    return Workload(name, 100, B, H, N, d, dtype, causal, key_bias_std, **kw)
+        return Workload(name, 100 + w.cfg_id, B, H, N, d, dtype, causal, Nk_=Nk, **params)
+    return Workload(name, 100, B, H, N, d, dtype, causal, key_bias_std, Nk_=Nk, **kw)
 
 
 def _rng(seed: int, w: Workload, *ids: int) -> np.random.Generator:
@@ -106,10 +117,11 @@ def failing_heads(w: Workload, seed: int = 0) -> np.ndarray:
 
 
 def outlier_rows(w: Workload, b: int, h: int, seed: int = 0) -> np.ndarray:
-    k = int(round(w.outlier_frac * w.N))
+    """Key rows scaled further on a failing head (a seeded 0.1% of them)."""
+    k = int(round(w.outlier_frac * w.Nk))
     if k == 0:
         return np.zeros(0, dtype=np.int64)
-    return np.sort(_rng(seed, w, b, h, 1_000_002).choice(w.N, size=k, replace=False).astype(np.int64))
+    return np.sort(_rng(seed, w, b, h, 1_000_002).choice(w.Nk, size=k, replace=False).astype(np.int64))
 
 
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -126,10 +138,10 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 def head_f32(w: Workload, b: int, h: int, seed: int = 0, fail_set=None):
     """Q, K, V of one (b, h) head as fp32 [N, d] arrays, before any rounding."""
-    N, d = w.N, w.d
-    q = _rng(seed, w, b, h, TENSOR_Q).standard_normal((N, d), dtype=np.float32)
-    k = _rng(seed, w, b, h, TENSOR_K).standard_normal((N, d), dtype=np.float32)
-    v = _rng(seed, w, b, h, TENSOR_V).standard_normal((N, d), dtype=np.float32)
+    d = w.d
+    q = _rng(seed, w, b, h, TENSOR_Q).standard_normal((w.Nq, d), dtype=np.float32)
+    k = _rng(seed, w, b, h, TENSOR_K).standard_normal((w.Nk, d), dtype=np.float32)
+    v = _rng(seed, w, b, h, TENSOR_V).standard_normal((w.Nk, d), dtype=np.float32)
     if w.key_bias_std:
         bias = _rng(seed, w, b, h, TENSOR_KBIAS).standard_normal(d, dtype=np.float32)
         k += np.float32(w.key_bias_std) * bias
@@ -155,8 +167,8 @@ def make_inputs(w: Workload, seed: int = 0, heads=None):
     the other heads are left zero (used only where a test needs a few heads).
     """
     out_dtype = np.uint16 if w.dtype == "bf16" else np.float32
-    shape = (w.B, w.H, w.N, w.d)
-    Q, K, V = (np.zeros(shape, dtype=out_dtype) for _ in range(3))
+    Q = np.zeros((w.B, w.H, w.Nq, w.d), dtype=out_dtype)
+    K, V = (np.zeros((w.B, w.H, w.Nk, w.d), dtype=out_dtype) for _ in range(2))
     fail_set = set(failing_heads(w, seed).tolist())
     todo = range(w.B * w.H) if heads is None else heads
 
