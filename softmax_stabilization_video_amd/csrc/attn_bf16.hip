@@ -5,125 +5,169 @@
 //             reduction and no accumulator rescaling ("CLiS: Plug-and-Play
 //             Attention Acceleration for Video Diffusion on TPUs via
 //             Certified Stabilization", abstract and Figure 5(a));
-//   ONLINE -- online softmax: per key tile a running row maximum, a rescale
-//             factor alpha for the row sum and the output accumulator (the
-//             baseline the same pages compare against).
+//   ONLINE -- online softmax: per key tile a running row maximum and a
+//             rescale factor alpha for the row sum and the output accumulator
+//             (the baseline those pages compare against).
 //
-// Work decomposition.  One workgroup = 4 waves = 128 query rows of one
-// (batch, head); each wave owns 32 rows.  Key/value tiles of 64 rows are
-// staged through LDS and shared by the 4 waves.  Both products use
+// Work decomposition.  A workgroup of kWaves waves owns kBM = 32*kWaves query
+// rows of one (batch, head); each wave owns 32 rows.  Key/value tiles of kBN
+// rows stream through a two-stage LDS ring: the tile after the current one is
+// loaded with direct global->LDS loads (global_load_lds_dwordx4) while the
+// current one is consumed, with one barrier per tile.  Both products use
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation, oriented so that every
 // lane owns one query row:
-//   S^T = K Q^T   A = K rows from LDS, B = Q fragments held in registers;
-//                 lane l holds scores of query l%32 for 16 of every 32 keys,
-//                 the other 16 sit in lane l^32.
-//   O^T = V^T P^T A = V^T from LDS, B = P taken straight from the S^T
-//                 accumulator registers (converted to bf16); lane l holds
-//                 query l%32's output for 16 of every 32 channels.
-// Per-row quantities (mu, m, l, alpha) are therefore per lane, and a row
-// needs a cross-lane step only between lanes l and l^32.
+//   S^T = K Q^T   A = K rows read from LDS (ds_read_b128), B = Q fragments
+//                 held in registers for the whole loop; lane l holds the
+//                 scores of query l%32 for 16 of every 32 keys (the other 16
+//                 sit in lane l^32).
+//   O^T = V^T P^T A = V^T fragments read from the row-major V tile with the
+//                 LDS transpose read ds_read_b64_tr_b16, B = P taken straight
+//                 from the S^T accumulators (converted to bf16).
+// Per-row quantities (mu, m, l, alpha) are therefore per lane; a row needs a
+// cross-lane step only between lanes l and l^32 (the online max per tile, and
+// the final row sum).
+//
+// LDS layouts.  Tiles are row-major with 16-byte chunks XOR-swizzled per row,
+// so the K operand reads (16 rows x 16 bytes per 16 lanes) and the V
+// transpose reads (4 rows x 64 bytes per 32 lanes) hit distinct banks.  The
+// swizzle is applied when loading: lane i of a direct-to-LDS load writes LDS
+// slot base+16i, so each lane fetches the global chunk that belongs there.
+// Rows past the last key are filled from a 16-byte zero source, so padded
+// keys hold zeros (their weights are also masked to 0).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
 #include "internal.h"
 
 namespace clis {
+
+// 16 zero bytes: the global source of LDS rows past the last key.
+__device__ uint4 g_zero_chunk;
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) short4v lds_short4;
 
 constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
+constexpr int kXcds = 8;          // MI355X: workgroups are dealt round-robin to 8 XCDs
 
 __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
-  return __builtin_bit_cast(bf16x8, u);
-}
-
-// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};  // round to nearest even
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Per-row 16-byte chunk swizzles (see the file comment).
+template <int D>
+__device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+
+// One wave's share of a kBN x D tile: direct global->LDS loads, swizzled.
+template <int D, bool IS_V>
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src, int kt, int Nk, uint16_t* tile,
+                                          int wave, int lane) {
+  constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  constexpr int INSTR = kBN * CPR / (64 * kWaves); // instructions per wave
+#pragma unroll
+  for (int j = 0; j < INSTR; ++j) {
+    const int slot0 = (j * kWaves + wave) * 64;
+    const int slot = slot0 + lane;
+    const int row = slot / CPR, p = slot % CPR;
+    const int c = p ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
+    const int key = kt + row;
+    const void* g = (key < Nk) ? static_cast<const void*>(src + (size_t)key * D + c * 8)
+                               : static_cast<const void*>(&g_zero_chunk);
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)(tile + slot0 * 8), 16, 0, 0);
+  }
+}
+
+// Logical block id for physical id `bid` when the first `active` blocks are
+// live: each XCD gets one contiguous range of logical ids, so the query tiles
+// of a head (which share its keys and values) stay within one XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int active) {
+  const int x = bid % kXcds, i = bid / kXcds;
+  const int base = active / kXcds, rem = active % kXcds;
+  return (x < rem) ? x * (base + 1) + i : rem * (base + 1) + (x - rem) * base + i;
+}
+
 template <int D, bool FIXED, bool CAUSAL>
-__global__ void __launch_bounds__(64 * kWaves)
+__global__ void __launch_bounds__(kThreads, 2)
 attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
               const float* __restrict__ mu, const int32_t* __restrict__ head_list,
-              const int32_t* __restrict__ head_count, int Nq, int Nk, float c2) {
-  constexpr int KP = D + 8;     // K tile row pitch (elements): 16 B pad per row
-  constexpr int VP = kBN + 8;   // V^T tile row pitch (elements)
-  constexpr int NS = D / 16;    // k-steps of the S product
-  constexpr int NC = D / 32;    // 32-channel blocks of the output
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+              const int32_t* __restrict__ head_count, int n_slots, int Nq, int Nk, float c2) {
+  constexpr int NS = D / 16;   // k-steps of the S product
+  constexpr int NC = D / 32;   // 32-channel blocks of the output
+  constexpr int TILE = kBN * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][TILE];  // [stage][K,V]
 
   const int n_qt = (Nq + kBM - 1) / kBM;
-  const int slot = blockIdx.x / n_qt;
-  int qt = blockIdx.x % n_qt;
+  const int active = (head_list ? *head_count : n_slots) * n_qt;
+  if ((int)blockIdx.x >= active) return;
+  const int lid = xcd_remap(blockIdx.x, active);
+  const int slot = lid / n_qt;
+  int qt = lid % n_qt;
   if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
-  int bh = slot;
-  if (head_list) {
-    if (slot >= *head_count) return;
-    bh = head_list[slot];
-  }
+  const int bh = head_list ? head_list[slot] : slot;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, ln = lane & 31;
-  const int qrow = qt * kBM + wave * 32 + ln;
+  const int row0 = qt * kBM + wave * 32;  // first query row of this wave
+  const int qrow = row0 + ln;
   const bool qvalid = qrow < Nq;
   const size_t qoff = ((size_t)bh * Nq + (qvalid ? qrow : 0)) * D;
   const uint16_t* Kh = K + (size_t)bh * Nk * D;
   const uint16_t* Vh = V + (size_t)bh * Nk * D;
+
+  const int kv_end = CAUSAL ? min(Nk, (qt + 1) * kBM) : Nk;
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+
+  // first tile in flight before anything else
+  load_tile<D, false>(Kh, 0, Nk, lds[0][0], wave, lane);
+  load_tile<D, true>(Vh, 0, Nk, lds[0][1], wave, lane);
 
   bf16x8 qf[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     uint4 u = make_uint4(0, 0, 0, 0);
     if (qvalid) u = *reinterpret_cast<const uint4*>(Q + qoff + 16 * s + 8 * g);
-    qf[s] = as_bf16x8(u);
+    qf[s] = __builtin_bit_cast(bf16x8, u);
   }
-
   float mrow = FIXED ? (qvalid ? mu[(size_t)bh * Nq + qrow] : 0.f) : -INFINITY;
-  float lsum = 0.f;
+  const float negmu = -mrow;
+  float lsum0 = 0.f, lsum1 = 0.f;
   floatx16 oacc[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[c][r] = 0.f;
 
-  const int kv_end = CAUSAL ? min(Nk, (qt + 1) * kBM) : Nk;
-  for (int kt = 0; kt < kv_end; kt += kBN) {
-    __syncthreads();  // the previous tile is no longer read
-    // ---- stage K (row-major) and V (transposed) tiles in LDS
-    constexpr int CH = D / 8;  // 16-byte chunks per row
-#pragma unroll
-    for (int it = 0; it < kBN * CH / (64 * kWaves); ++it) {
-      const int id = tid + it * 64 * kWaves;
-      const int r = id / CH, ch = id % CH;
-      const int key = kt + r;
-      uint4 ku = make_uint4(0, 0, 0, 0), vu = make_uint4(0, 0, 0, 0);
-      if (key < Nk) {
-        ku = *reinterpret_cast<const uint4*>(Kh + (size_t)key * D + ch * 8);
-        vu = *reinterpret_cast<const uint4*>(Vh + (size_t)key * D + ch * 8);
-      }
-      *reinterpret_cast<uint4*>(&Ks[r * KP + ch * 8]) = ku;
-      const uint32_t w[4] = {vu.x, vu.y, vu.z, vu.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(ch * 8 + 2 * e) * VP + r] = (uint16_t)(w[e] & 0xffffu);
-        Vt[(ch * 8 + 2 * e + 1) * VP + r] = (uint16_t)(w[e] >> 16);
-      }
+  // lane coordinates of the transpose reads: 16-lane group G = lane/16
+  const int tr_r = (lane & 15) >> 2, tr_q = lane & 3, tr_hc = (lane >> 4) & 1;
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int kt = it * kBN;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile `it` is in LDS; nobody still reads the other stage
+    if (it + 1 < ntiles) {
+      load_tile<D, false>(Kh, kt + kBN, Nk, lds[(it + 1) & 1][0], wave, lane);
+      load_tile<D, true>(Vh, kt + kBN, Nk, lds[(it + 1) & 1][1], wave, lane);
     }
-    __syncthreads();
+    if (CAUSAL && kt > row0 + 31) continue;  // every key of the tile is above this wave's rows
+    const uint16_t* Ks = lds[it & 1][0];
+    const uint16_t* Vs = lds[it & 1][1];
 
     // ---- S^T = K Q^T for two 32-key blocks
     floatx16 sacc[2];
@@ -131,52 +175,70 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      const int row = kb * 32 + ln;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[(kb * 32 + ln) * KP + 16 * s + 8 * g]));
+        const int phys = (2 * s + g) ^ swz_k<D>(row);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + row * D + phys * 8);
         sacc[kb] = mfma32(a, qf[s], sacc[kb]);
       }
     }
 
     // ---- exp2 weights.  Register r of block kb holds key
     //      kt + 32 kb + 8 (r / 4) + 4 g + r % 4.
+    const bool need_mask = (kt + kBN > Nk) || (CAUSAL && kt + kBN - 1 > row0);
     float p[2][16];
     if constexpr (FIXED) {
+      if (!need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = key < Nk && (!CAUSAL || key <= qrow);
-          const float x = ok ? fmaf(sacc[kb][r], c2, -mrow) : -INFINITY;
-          p[kb][r] = __builtin_amdgcn_exp2f(x);
-          lsum += p[kb][r];
-        }
+          for (int r = 0; r < 16; ++r) p[kb][r] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, negmu));
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const bool ok = key < Nk && (!CAUSAL || key <= qrow);
+            p[kb][r] = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, negmu)) : 0.f;
+          }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        lsum0 += p[0][r];
+        lsum1 += p[1][r];
+      }
     } else {
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = key < Nk && (!CAUSAL || key <= qrow);
-          p[kb][r] = ok ? sacc[kb][r] * c2 : -INFINITY;
-          tmax = fmaxf(tmax, p[kb][r]);
+          float x = sacc[kb][r] * c2;
+          if (need_mask) {
+            const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const bool ok = key < Nk && (!CAUSAL || key <= qrow);
+            x = ok ? x : -INFINITY;
+          }
+          p[kb][r] = x;
+          tmax = fmaxf(tmax, x);
         }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
       const float mnew = fmaxf(mrow, tmax);
       const bool none = (mnew == -INFINITY);  // no visible key yet
       const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(mrow - mnew);
       const float msub = none ? 0.f : mnew;
-      float psum = 0.f;
+      float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[kb][r] = __builtin_amdgcn_exp2f(p[kb][r] - msub);
-          psum += p[kb][r];
-        }
-      lsum = fmaf(lsum, alpha, psum);
+      for (int r = 0; r < 16; ++r) {
+        p[0][r] = __builtin_amdgcn_exp2f(p[0][r] - msub);
+        p[1][r] = __builtin_amdgcn_exp2f(p[1][r] - msub);
+        ps0 += p[0][r];
+        ps1 += p[1][r];
+      }
+      lsum0 = fmaf(lsum0, alpha, ps0);
+      lsum1 = fmaf(lsum1, alpha, ps1);
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -195,19 +257,26 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         pu.y = pack_bf16(p[kb][8 * t + 2], p[kb][8 * t + 3]);
         pu.z = pack_bf16(p[kb][8 * t + 4], p[kb][8 * t + 5]);
         pu.w = pack_bf16(p[kb][8 * t + 6], p[kb][8 * t + 7]);
-        const bf16x8 pf = as_bf16x8(pu);
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, pu);
+        const int rlo = kb * 32 + 16 * t + 4 * g + tr_r;  // rows of the first half
+        const int rhi = rlo + 8;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const uint16_t* vr = &Vt[(c * 32 + ln) * VP + kb * 32 + 16 * t + 4 * g];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-          const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+          const int chunk = 4 * c + 2 * tr_hc + (tr_q >> 1);
+          const int off = 4 * (tr_q & 1);
+          const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_short4*)(Vs + rlo * D + (chunk ^ swz_v<D>(rlo)) * 8 + off));
+          const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_short4*)(Vs + rhi * D + (chunk ^ swz_v<D>(rhi)) * 8 + off));
+          const short4v both[2] = {lo, hi};
+          const bf16x8 a = __builtin_bit_cast(bf16x8, both);
           oacc[c] = mfma32(a, pf, oacc[c]);
         }
       }
   }
 
   // ---- epilogue: the row sum's two halves meet, then O = O_acc / l
+  float lsum = lsum0 + lsum1;
   lsum += __shfl_xor(lsum, 32);
   const float inv = 1.f / lsum;
   if (qvalid) {
@@ -229,10 +298,10 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   const int n_qt = (a.Nq + kBM - 1) / kBM;
   const long long blocks = (long long)n_qt * a.n_slots;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  attn_fwd_bf16<D, FIXED, CAUSAL><<<(unsigned)blocks, 64 * kWaves, 0, s>>>(
+  attn_fwd_bf16<D, FIXED, CAUSAL><<<(unsigned)blocks, kThreads, 0, s>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
       static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.mu, a.head_list,
-      a.head_count, a.Nq, a.Nk, a.c2);
+      a.head_count, a.n_slots, a.Nq, a.Nk, a.c2);
   return hipGetLastError();
 }
 

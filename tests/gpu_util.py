@@ -14,12 +14,8 @@ def say(*args):
 
 
 def to_device(a: np.ndarray, dtype: str):
-    import torch
-    if dtype == "bf16":
-        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
-    else:
-        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
-    return t.cuda()
+    import workloads
+    return workloads.to_torch(a, dtype, "cuda")
 
 
 def to_f64(t) -> np.ndarray:

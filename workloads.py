@@ -193,3 +193,14 @@ def sample_rows(w: Workload, n_random: int = 200, seed: int = 0, tiles=(64, 128,
     rng = _rng(seed, w, 1_000_003)
     rows.update(rng.choice(N, size=min(n_random, N), replace=False).tolist())
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def to_torch(a: np.ndarray, dtype: str, device: str = "cuda"):
+    """Copy seeded host inputs to a torch device tensor, bytes unchanged
+    (bf16 bit patterns become a bfloat16 tensor)."""
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device)
