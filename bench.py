@@ -132,6 +132,9 @@ def main(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", choices=["all", "clis", "online", "certify"], default="all",
                    help="restrict the extra timings (for profiler runs)")
+    p.add_argument("--reps", type=int, default=20, help="calls per extra timing")
+    p.add_argument("--calibrate-copy-mb", type=float, default=0.0,
+                   help="also run one plain device copy of this many MiB (scales HBM counters)")
     args = p.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -172,7 +175,7 @@ def main(argv=None):
     wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
     log(f"step (certify + attention): {ms_step:.3f} ms")
-    step_events = time_calls(step, max(5, min(args.steps, 20)), stream)
+    step_events = time_calls(step, max(1, min(args.steps, args.reps)), stream)
 
     mu, cert = clis.clis_certify(q, k, v, w.scale, workspace=ws)
     torch.cuda.synchronize()
@@ -180,19 +183,29 @@ def main(argv=None):
     res = {}
     if args.only in ("all", "clis"):
         kern = time_calls(lambda: clis.clis_attn_fwd(q, k, v, w.scale, w.causal, mode="auto", mu=mu,
-                                                     cert=cert, out=o, workspace=ws), 20, stream)
+                                                     cert=cert, out=o, workspace=ws), args.reps, stream)
         res["clis_kernel_ms"] = statistics.median(kern)
         # the dominant kernel on its own: every head on the fixed-stabilizer kernel
         fixed = time_calls(lambda: clis.clis_attn_fwd(q, k, v, w.scale, w.causal, mode="fixed", mu=mu,
-                                                      out=o, workspace=ws), 20, stream)
+                                                      out=o, workspace=ws), args.reps, stream)
         res["fixed_kernel_ms_mean"] = statistics.mean(fixed)
         res["fixed_kernel_ms_median"] = statistics.median(fixed)
     if args.only in ("all", "online"):
-        onl = time_calls(lambda: clis.online_attn_fwd(q, k, v, w.scale, w.causal, out=o), 20, stream)
+        onl = time_calls(lambda: clis.online_attn_fwd(q, k, v, w.scale, w.causal, out=o), args.reps, stream)
         res["online_ms"] = statistics.median(onl)
     if args.only in ("all", "certify"):
-        cer = time_calls(lambda: clis.clis_certify(q, k, v, w.scale, workspace=ws), 20, stream)
+        cer = time_calls(lambda: clis.clis_certify(q, k, v, w.scale, workspace=ws), args.reps, stream)
         res["certify_ms"] = statistics.median(cer)
+
+    if args.calibrate_copy_mb > 0:
+        nbytes = int(args.calibrate_copy_mb * 2 ** 20)
+        src = torch.ones(nbytes, dtype=torch.uint8, device=q.device)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # one plain copy kernel: reads and writes nbytes
+        torch.cuda.synchronize()
+        log(f"calibration copy of {nbytes} bytes done")
+        del src, dst
 
     value = flops / (ms_step * 1e-3) / 1e12
     out = {

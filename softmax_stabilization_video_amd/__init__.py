@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
     clis_attn_fwd(q, k, v, ...)        -> o            (mode auto/fixed/online)
     online_attn_fwd(q, k, v, ...)      -> o
 Tensors are [B, H, N, d], contiguous, bf16 or fp32, on the GPU.
+The library is loaded on first use; a missing build raises ImportError.
 
 Method: "CLiS: Plug-and-Play Attention Acceleration for Video Diffusion on
 TPUs via Certified Stabilization" (abstract; Algorithm 1).
@@ -66,12 +67,26 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     return L
 
 
-lib = load_library()
+_lib = None
+
+
+def get_lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        _lib = load_library()
+    return _lib
+
+
+def __getattr__(name):  # module attribute `lib`, loaded on first access
+    if name == "lib":
+        return get_lib()
+    raise AttributeError(name)
 
 
 def _check(status: int):
     if status != 0:
-        raise ClisError(status, lib.clis_last_error().decode())
+        raise ClisError(status, get_lib().clis_last_error().decode())
 
 
 def _ptr(t):
@@ -106,7 +121,7 @@ def _shapes(q, k, v):
 
 
 def workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
-    return int(lib.clis_workspace_bytes(B, H, Nq, Nk, d))
+    return int(get_lib().clis_workspace_bytes(B, H, Nq, Nk, d))
 
 
 def new_workspace(B: int, H: int, Nq: int, Nk: int, d: int, device=None):
@@ -132,7 +147,7 @@ def clis_certify(q, k, v, scale: float | None = None, *, want_stats: bool = Fals
         stats = torch.empty((B * H, STATS_BYTES), dtype=torch.uint8, device=q.device)
         kbar = torch.empty((B, H, d), dtype=torch.float64, device=q.device)
     ws = workspace if workspace is not None else new_workspace(B, H, Nq, Nk, d, q.device)
-    _check(lib.clis_certify(_ptr(q), _ptr(k), _ptr(v), B, H, Nq, Nk, d, scale, _dtype_code(q),
+    _check(get_lib().clis_certify(_ptr(q), _ptr(k), _ptr(v), B, H, Nq, Nk, d, scale, _dtype_code(q),
                             _ptr(mu), _ptr(cert), _ptr(stats), _ptr(kbar), _ptr(ws), ws.numel(),
                             _stream(stream)))
     return (mu, cert, stats, kbar) if want_stats else (mu, cert)
@@ -156,7 +171,7 @@ def clis_attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, mod
     ws = workspace
     if ws is None and (mode != "online" or want_route):
         ws = new_workspace(B, H, Nq, Nk, d, q.device)
-    _check(lib.clis_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Nq, Nk, d, scale, int(causal),
+    _check(get_lib().clis_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Nq, Nk, d, scale, int(causal),
                              _dtype_code(q), MODES[mode], _ptr(mu), _ptr(cert), _ptr(route), _ptr(ws),
                              0 if ws is None else ws.numel(), _stream(stream)))
     return (o, route) if want_route else o
@@ -168,7 +183,7 @@ def online_attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, o
     B, H, Nq, Nk, d = _shapes(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
-    _check(lib.online_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Nq, Nk, d, scale, int(causal),
+    _check(get_lib().online_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Nq, Nk, d, scale, int(causal),
                                _dtype_code(q), _stream(stream)))
     return o
 

@@ -46,6 +46,13 @@ def build(verbose: bool = False, extra=()) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # every kernel launched from host code must have its host stub defined;
+    # a silently dropped kernel instantiation shows up as an undefined symbol
+    nm = subprocess.run(["nm", "-C", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.strip() for l in nm.stdout.splitlines() if "clis::" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("libclis.so has undefined library symbols:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

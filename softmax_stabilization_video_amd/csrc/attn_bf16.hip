@@ -12,8 +12,8 @@
 // Work decomposition.  A workgroup of kWaves waves owns kBM = 32*kWaves query
 // rows of one (batch, head); each wave owns 32 rows.  Key/value tiles of kBN
 // rows stream through a two-stage LDS ring: the tile after the current one is
-// loaded with direct global->LDS loads (global_load_lds_dwordx4) while the
-// current one is consumed, with one barrier per tile.  Both products use
+// loaded with buffer loads that write LDS directly (buffer_load_dwordx4 ...
+// lds) while the current one is consumed, with one barrier per tile.  Both products use
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation, oriented so that every
 // lane owns one query row:
 //   S^T = K Q^T   A = K rows read from LDS (ds_read_b128), B = Q fragments
@@ -30,19 +30,18 @@
 // LDS layouts.  Tiles are row-major with 16-byte chunks XOR-swizzled per row,
 // so the K operand reads (16 rows x 16 bytes per 16 lanes) and the V
 // transpose reads (4 rows x 64 bytes per 32 lanes) hit distinct banks.  The
-// swizzle is applied when loading: lane i of a direct-to-LDS load writes LDS
-// slot base+16i, so each lane fetches the global chunk that belongs there.
-// Rows past the last key are filled from a 16-byte zero source, so padded
-// keys hold zeros (their weights are also masked to 0).
+// swizzle is applied when loading: lane i of a load-to-LDS instruction writes
+// LDS slot base+16i, so each lane fetches the global chunk that belongs there.
+// Rows past the last key read as zeros (the buffer descriptor's range check),
+// and their weights are masked to 0.
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "internal.h"
 
 namespace clis {
-
-// 16 zero bytes: the global source of LDS rows past the last key.
-__device__ uint4 g_zero_chunk;
 
 namespace {
 
@@ -57,6 +56,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr int kXcds = 8;          // MI355X: workgroups are dealt round-robin to 8 XCDs
+constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor word 3 (untyped 32-bit data)
 
 __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -74,25 +74,6 @@ __device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : (
 template <int D>
 __device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
-// One wave's share of a kBN x D tile: direct global->LDS loads, swizzled.
-template <int D, bool IS_V>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src, int kt, int Nk, uint16_t* tile,
-                                          int wave, int lane) {
-  constexpr int CPR = D / 8;                       // 16-byte chunks per row
-  constexpr int INSTR = kBN * CPR / (64 * kWaves); // instructions per wave
-#pragma unroll
-  for (int j = 0; j < INSTR; ++j) {
-    const int slot0 = (j * kWaves + wave) * 64;
-    const int slot = slot0 + lane;
-    const int row = slot / CPR, p = slot % CPR;
-    const int c = p ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
-    const int key = kt + row;
-    const void* g = (key < Nk) ? static_cast<const void*>(src + (size_t)key * D + c * 8)
-                               : static_cast<const void*>(&g_zero_chunk);
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)(tile + slot0 * 8), 16, 0, 0);
-  }
-}
-
 // Logical block id for physical id `bid` when the first `active` blocks are
 // live: each XCD gets one contiguous range of logical ids, so the query tiles
 // of a head (which share its keys and values) stay within one XCD's L2.
@@ -102,16 +83,47 @@ __device__ __forceinline__ int xcd_remap(int bid, int active) {
   return (x < rem) ? x * (base + 1) + i : rem * (base + 1) + (x - rem) * base + i;
 }
 
+template <int D>
+struct Geometry {
+  static constexpr int NS = D / 16;                      // k-steps of the S product
+  static constexpr int NC = D / 32;                      // 32-channel output blocks
+  static constexpr int CPR = D / 8;                      // 16-byte chunks per tile row
+  static constexpr int TILE_BYTES = kBN * D * 2;         // one K or V tile
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;     // K then V
+  static constexpr int LOADS = kBN * CPR / kThreads;     // direct loads per lane per tile
+};
+
+// One wave's share of the K and V tiles starting at key kt: buffer loads that
+// write LDS directly (lane i -> slot base+16i).  The descriptors cover only
+// the rows that exist, so lanes past the last key read zeros without touching
+// memory.  gk/gv are the lanes' swizzled source offsets within a tile.
+template <int D>
+__device__ __forceinline__ void load_kv_tile(const char* Kh, const char* Vh, int kt, int Nk, char* stage,
+                                             int wave, const uint32_t* gk, const uint32_t* gv) {
+  using G = Geometry<D>;
+  char* kdst = stage + wave * 1024;
+  char* vdst = kdst + G::TILE_BYTES;
+  const int bytes = min(Nk - kt, kBN) * D * 2;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Kh + (size_t)kt * D * 2), 0, bytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Vh + (size_t)kt * D * 2), 0, bytes, kBufferFlags);
+#pragma unroll
+  for (int j = 0; j < G::LOADS; ++j) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kdst + j * kThreads * 16), 16, gk[j], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + j * kThreads * 16), 16, gv[j], 0, 0, 0);
+  }
+}
+
 template <int D, bool FIXED, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
               const float* __restrict__ mu, const int32_t* __restrict__ head_list,
               const int32_t* __restrict__ head_count, int n_slots, int Nq, int Nk, float c2) {
-  constexpr int NS = D / 16;   // k-steps of the S product
-  constexpr int NC = D / 32;   // 32-channel blocks of the output
-  constexpr int TILE = kBN * D;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][TILE];  // [stage][K,V]
+  using G = Geometry<D>;
+  constexpr int NS = G::NS, NC = G::NC;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * G::STAGE_BYTES];  // [stage][K tile, V tile]
 
   const int n_qt = (Nq + kBM - 1) / kBM;
   const int active = (head_list ? *head_count : n_slots) * n_qt;
@@ -122,21 +134,47 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
   const int bh = head_list ? head_list[slot] : slot;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, ln = lane & 31;
   const int row0 = qt * kBM + wave * 32;  // first query row of this wave
   const int qrow = row0 + ln;
   const bool qvalid = qrow < Nq;
   const size_t qoff = ((size_t)bh * Nq + (qvalid ? qrow : 0)) * D;
-  const uint16_t* Kh = K + (size_t)bh * Nk * D;
-  const uint16_t* Vh = V + (size_t)bh * Nk * D;
+  const char* Kh = reinterpret_cast<const char*>(K + (size_t)bh * Nk * D);
+  const char* Vh = reinterpret_cast<const char*>(V + (size_t)bh * Nk * D);
 
   const int kv_end = CAUSAL ? min(Nk, (qt + 1) * kBM) : Nk;
   const int ntiles = (kv_end + kBN - 1) / kBN;
 
+  // ---- per-lane, loop-invariant offsets
+  // direct loads: lane slot -> (tile row, physical chunk) -> swizzled source chunk
+  uint32_t gk[G::LOADS], gv[G::LOADS];
+#pragma unroll
+  for (int j = 0; j < G::LOADS; ++j) {
+    const int s = (j * kWaves + wave) * 64 + lane;
+    const int row = s / G::CPR, p = s % G::CPR;
+    gk[j] = (uint32_t)(row * D + (p ^ swz_k<D>(row)) * 8) * 2;
+    gv[j] = (uint32_t)(row * D + (p ^ swz_v<D>(row)) * 8) * 2;
+  }
+  // K operand reads: row ln of a 32-key block, chunk 2s+g, swizzled
+  uint32_t kro[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) kro[s] = (uint32_t)(ln * D + (((2 * s + g) ^ swz_k<D>(ln)) * 8)) * 2;
+  // V transpose reads: 16-lane group supplies 4 rows x 16 channels
+  const int tr_r = (lane & 15) >> 2, tr_q = lane & 3, tr_hc = (lane >> 4) & 1;
+  uint32_t vro[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    vro[c] = (uint32_t)((4 * g + tr_r) * D + ((4 * c + 2 * tr_hc + (tr_q >> 1)) ^ swz_v<D>(tr_r)) * 8 +
+                        4 * (tr_q & 1)) * 2;
+
+  auto load_tile = [&](int kt, int stage) {
+    load_kv_tile<D>(Kh, Vh, kt, Nk, lds + stage * G::STAGE_BYTES, wave, gk, gv);
+  };
+
   // first tile in flight before anything else
-  load_tile<D, false>(Kh, 0, Nk, lds[0][0], wave, lane);
-  load_tile<D, true>(Vh, 0, Nk, lds[0][1], wave, lane);
+  load_tile(0, 0);
 
   bf16x8 qf[NS];
 #pragma unroll
@@ -147,41 +185,38 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
   float mrow = FIXED ? (qvalid ? mu[(size_t)bh * Nq + qrow] : 0.f) : -INFINITY;
   const float negmu = -mrow;
-  float lsum0 = 0.f, lsum1 = 0.f;
+  float lsum = 0.f;
   floatx16 oacc[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[c][r] = 0.f;
 
-  // lane coordinates of the transpose reads: 16-lane group G = lane/16
-  const int tr_r = (lane & 15) >> 2, tr_q = lane & 3, tr_hc = (lane >> 4) & 1;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  for (int it = 0; it < ntiles; ++it) {
+  auto tile = [&](int it, auto stage_tag) {
+    constexpr int ST = decltype(stage_tag)::value;
     const int kt = it * kBN;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // tile `it` is in LDS; nobody still reads the other stage
-    if (it + 1 < ntiles) {
-      load_tile<D, false>(Kh, kt + kBN, Nk, lds[(it + 1) & 1][0], wave, lane);
-      load_tile<D, true>(Vh, kt + kBN, Nk, lds[(it + 1) & 1][1], wave, lane);
-    }
-    if (CAUSAL && kt > row0 + 31) continue;  // every key of the tile is above this wave's rows
-    const uint16_t* Ks = lds[it & 1][0];
-    const uint16_t* Vs = lds[it & 1][1];
+    if (it + 1 < ntiles) load_tile(kt + kBN, ST ^ 1);
+    if (CAUSAL && kt > row0 + 31) return;  // every key of the tile is above this wave's rows
+    const char* Ks = lds + ST * G::STAGE_BYTES;
+    const char* Vs = Ks + G::TILE_BYTES;
 
     // ---- S^T = K Q^T for two 32-key blocks
     floatx16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-      const int row = kb * 32 + ln;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int phys = (2 * s + g) ^ swz_k<D>(row);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + row * D + phys * 8);
-        sacc[kb] = mfma32(a, qf[s], sacc[kb]);
-      }
+    for (int s = 0; s < NS; ++s) {  // the two blocks' chains alternate
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(Ks + kro[s]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(Ks + 32 * D * 2 + kro[s]);
+      sacc[0] = mfma32(a0, qf[s], sacc[0]);
+      sacc[1] = mfma32(a1, qf[s], sacc[1]);
     }
 
     // ---- exp2 weights.  Register r of block kb holds key
@@ -204,11 +239,6 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             p[kb][r] = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, negmu)) : 0.f;
           }
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        lsum0 += p[0][r];
-        lsum1 += p[1][r];
-      }
     } else {
       float tmax = -INFINITY;
 #pragma unroll
@@ -229,16 +259,11 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const bool none = (mnew == -INFINITY);  // no visible key yet
       const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(mrow - mnew);
       const float msub = none ? 0.f : mnew;
-      float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[0][r] = __builtin_amdgcn_exp2f(p[0][r] - msub);
-        p[1][r] = __builtin_amdgcn_exp2f(p[1][r] - msub);
-        ps0 += p[0][r];
-        ps1 += p[1][r];
-      }
-      lsum0 = fmaf(lsum0, alpha, ps0);
-      lsum1 = fmaf(lsum1, alpha, ps1);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[kb][r] = __builtin_amdgcn_exp2f(p[kb][r] - msub);
+      lsum *= alpha;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -247,36 +272,36 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
 
     // ---- O^T += V^T P^T.  k-step t of block kb covers registers 8t..8t+7,
-    //      i.e. keys 32 kb + 16 t + {4g..4g+3, 8+4g..8+4g+3}.
+    //      i.e. keys 32 kb + 16 t + {4g..4g+3, 8+4g..8+4g+3}.  The row sum
+    //      adds the same bf16-rounded weights that enter the product.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        uint4 pu;
-        pu.x = pack_bf16(p[kb][8 * t + 0], p[kb][8 * t + 1]);
-        pu.y = pack_bf16(p[kb][8 * t + 2], p[kb][8 * t + 3]);
-        pu.z = pack_bf16(p[kb][8 * t + 4], p[kb][8 * t + 5]);
-        pu.w = pack_bf16(p[kb][8 * t + 6], p[kb][8 * t + 7]);
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, pu);
-        const int rlo = kb * 32 + 16 * t + 4 * g + tr_r;  // rows of the first half
-        const int rhi = rlo + 8;
+        uint32_t pw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pw[e] = pack_bf16(p[kb][8 * t + 2 * e], p[kb][8 * t + 2 * e + 1]);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), ones, lsum, false);
+        }
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+        const int rbase = (kb * 32 + 16 * t) * D * 2;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const int chunk = 4 * c + 2 * tr_hc + (tr_q >> 1);
-          const int off = 4 * (tr_q & 1);
-          const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_short4*)(Vs + rlo * D + (chunk ^ swz_v<D>(rlo)) * 8 + off));
-          const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_short4*)(Vs + rhi * D + (chunk ^ swz_v<D>(rhi)) * 8 + off));
+          const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(Vs + rbase + vro[c]));
+          const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(Vs + rbase + 8 * D * 2 + vro[c]));
           const short4v both[2] = {lo, hi};
-          const bf16x8 a = __builtin_bit_cast(bf16x8, both);
-          oacc[c] = mfma32(a, pf, oacc[c]);
+          oacc[c] = mfma32(__builtin_bit_cast(bf16x8, both), pf, oacc[c]);
         }
       }
+  };
+
+  for (int it = 0; it < ntiles; it += 2) {
+    tile(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntiles) tile(it + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: the row sum's two halves meet, then O = O_acc / l
-  float lsum = lsum0 + lsum1;
   lsum += __shfl_xor(lsum, 32);
   const float inv = 1.f / lsum;
   if (qvalid) {
