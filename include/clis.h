@@ -36,7 +36,8 @@
  * Shapes.  d must be 64 or 128.  B, H, Nq may be 0 (nothing is enqueued and
  * CLIS_OK is returned); a call with at least one query row needs Nk >= 1.
  * causal needs Nq == Nk (query i sees keys 0..i).  scale must be finite and
- * > 0.  Every dimension must fit in int32, and B*H*N*d in int64.
+ * > 0.  Every dimension must fit in int32, B*H*N*d in int64, and one head's
+ * keys must span less than 2 GiB (d * Nk * 2 bytes, Nk rounded up to 64).
  */
 #ifndef CLIS_H
 #define CLIS_H
@@ -83,7 +84,8 @@ typedef struct {
 } clis_head_stats_t;
 
 /* Workspace bytes any entry point of this library needs for these shapes
- * (the certification scratch plus stabilizers, flags and route lists). */
+ * (the certification scratch, stabilizers, flags, route lists, and a
+ * transposed copy of V for the bf16 attention kernels). */
 size_t clis_workspace_bytes(int B, int H, int Nq, int Nk, int d);
 
 /*
@@ -125,7 +127,7 @@ int clis_certify(const void* q, const void* k, const void* v,
  *              certification runs first inside this call, into ws.
  *   route_out  device [B, H] int32 (1 fixed, 0 online), or NULL.
  *   ws         device workspace (clis_workspace_bytes()); may be NULL only if
- *              mode is online.
+ *              mode is online and dtype is fp32.
  * Output dtype equals input dtype: fp32 accumulation, bf16 stored with round
  * to nearest even; on the bf16 path the exp2 weights are rounded to bf16
  * (nearest even) before the P.V product.
@@ -140,11 +142,13 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o,
  * fallback path [CLiS abstract: running row maxima and accumulator
  * rescaling].  Per key tile: m' = max(m, tile max of c*s), alpha = 2^{m-m'},
  * l = alpha*l + sum 2^{c*s-m'}, O = alpha*O + P.V.  Bitwise equal to
- * clis_attn_fwd with CLIS_MODE_ONLINE.  Needs no workspace.
+ * clis_attn_fwd with CLIS_MODE_ONLINE.  The bf16 kernels read V through a
+ * transposed copy kept in ws (clis_workspace_bytes()); ws may be NULL for
+ * fp32.
  */
 int online_attn_fwd(const void* q, const void* k, const void* v, void* o,
                     int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
-                    void* stream);
+                    void* ws, size_t ws_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* clis_status_string(int status);

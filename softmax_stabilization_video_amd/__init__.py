@@ -57,7 +57,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.clis_workspace_bytes.restype = sz
     L.clis_certify.argtypes = [vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, vp, vp, sz, vp]
     L.clis_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp, vp, vp, sz, vp]
-    L.online_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    L.online_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     for fn in (L.clis_certify, L.clis_attn_fwd, L.online_attn_fwd, L.clis_abi_version):
         fn.restype = ctypes.c_int
     L.clis_status_string.argtypes = [i]
@@ -169,7 +169,7 @@ def clis_attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, mod
         raise ValueError("out must be a contiguous tensor like q")
     route = torch.empty((B, H), dtype=torch.int32, device=q.device) if want_route else None
     ws = workspace
-    if ws is None and (mode != "online" or want_route):
+    if ws is None and (mode != "online" or want_route or q.dtype != torch.float32):
         ws = new_workspace(B, H, Nq, Nk, d, q.device)
     _check(get_lib().clis_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Nq, Nk, d, scale, int(causal),
                              _dtype_code(q), MODES[mode], _ptr(mu), _ptr(cert), _ptr(route), _ptr(ws),
@@ -177,14 +177,18 @@ def clis_attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, mod
     return (o, route) if want_route else o
 
 
-def online_attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, stream=None):
+def online_attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, workspace=None,
+                    stream=None):
     """Online-softmax attention forward for every head (online_attn_fwd)."""
     import torch
     B, H, Nq, Nk, d = _shapes(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
+    ws = workspace
+    if ws is None and q.dtype != torch.float32:
+        ws = new_workspace(B, H, Nq, Nk, d, q.device)
     _check(get_lib().online_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Nq, Nk, d, scale, int(causal),
-                               _dtype_code(q), _stream(stream)))
+                                     _dtype_code(q), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return o
 
 

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libclis.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "certify.hip", "attn_bf16.hip", "attn_fp32.hip"]
+SOURCES = ["api.hip", "certify.hip", "attn_bf16.hip", "attn_bf16_r64.hip", "attn_fp32.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -28,8 +28,8 @@ CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src: str, extra=()) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra=(), tag: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
     cmd = [HIPCC, *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -37,11 +37,14 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
+    """Compile every source and link `out` (default: the package's libclis.so;
+    `extra` adds compiler flags, e.g. -D tuning knobs for a variant library)."""
     os.makedirs(BUILD, exist_ok=True)
+    tag = "" if out == LIB else "." + os.path.basename(out).replace(".so", "")
     with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + f".tmp{os.getpid()}"
+        objs = list(ex.map(lambda s: _compile(s, extra, tag), SOURCES))
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -53,10 +56,10 @@ def build(verbose: bool = False, extra=()) -> str:
     if missing:
         os.remove(tmp)
         raise RuntimeError("libclis.so has undefined library symbols:\n" + "\n".join(missing))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -43,6 +43,8 @@ int check_common(int B, int H, int Nq, int Nk, int d, float scale, int dtype, in
   if (BH > 0x7fffffffLL) return fail(CLIS_ERR_SHAPE, "B*H exceeds int32");
   const long long nmax = Nq > Nk ? Nq : Nk;
   if (BH * nmax > (0x7fffffffffffffffLL / 4) / d) return fail(CLIS_ERR_SHAPE, "tensor too large");
+  if ((long long)d * clis::vt_pad(Nk) * 2 >= 0x7fffffffLL)
+    return fail(CLIS_ERR_SHAPE, "Nk=%d too large: one head's keys must span < 2 GiB", Nk);
   return CLIS_OK;
 }
 
@@ -100,9 +102,18 @@ clis::AttnArgs attn_args(const void* q, const void* k, const void* v, void* o, i
   return a;
 }
 
-hipError_t launch_attn(const clis::AttnArgs& a, int dtype, bool fixed, hipStream_t s) {
-  return dtype == CLIS_BF16 ? clis::launch_attn_bf16(a, fixed, s) : clis::launch_attn_fp32(a, fixed, s);
+// bf16 attention: 64 query rows per wave over a transposed V copy (default),
+// or the 32-rows-per-wave kernel that reads V directly.
+#ifndef CLIS_ATTN_ROWS
+#define CLIS_ATTN_ROWS 64
+#endif
+
+hipError_t launch_attn(const clis::AttnArgs& a, int dtype, bool fixed, const void* vt, hipStream_t s) {
+  if (dtype != CLIS_BF16) return clis::launch_attn_fp32(a, fixed, s);
+  return CLIS_ATTN_ROWS == 64 ? clis::launch_attn_bf16_r64(a, fixed, vt, s) : clis::launch_attn_bf16(a, fixed, s);
 }
+
+bool needs_vt(int dtype) { return dtype == CLIS_BF16 && CLIS_ATTN_ROWS == 64; }
 
 }  // namespace
 
@@ -139,14 +150,22 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
   if ((st = check_io(q, k, v, o, true)) != CLIS_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   clis::AttnArgs a = attn_args(q, k, v, o, B, H, Nq, Nk, d, scale, causal);
-
-  if (mode == CLIS_MODE_ONLINE && !route_out) {
-    const hipError_t e = launch_attn(a, dtype, false, s);
-    return e == hipSuccess ? CLIS_OK : hip_fail(e, "online attention launch");
+  const bool plain_online = (mode == CLIS_MODE_ONLINE && !route_out);
+  if (!plain_online || needs_vt(dtype)) {
+    if ((st = check_ws(ws, ws_bytes, B, H, Nq, Nk, d)) != CLIS_OK) return st;
   }
-  if ((st = check_ws(ws, ws_bytes, B, H, Nq, Nk, d)) != CLIS_OK) return st;
   const clis::WsLayout L = clis::ws_layout(B, H, Nq, Nk, d);
   const int BH = B * H;
+  hipError_t e;
+  void* vt = nullptr;
+  if (needs_vt(dtype)) {
+    vt = at<void>(ws, L.vt);
+    if ((e = clis::launch_transpose_v(v, vt, BH, Nk, d, s)) != hipSuccess) return hip_fail(e, "V transpose launch");
+  }
+  if (plain_online) {
+    e = launch_attn(a, dtype, false, vt, s);
+    return e == hipSuccess ? CLIS_OK : hip_fail(e, "online attention launch");
+  }
 
   const bool need_cert = (mode == CLIS_MODE_AUTO && (!cert || !mu)) || (mode == CLIS_MODE_FIXED && !mu);
   const float* mu_use = mu;
@@ -161,7 +180,7 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
   }
   int32_t* lists = at<int32_t>(ws, L.lists);
   int32_t* counts = at<int32_t>(ws, L.counts);
-  hipError_t e = clis::launch_route(cert_use, mode, BH, lists, counts, route_out, s);
+  e = clis::launch_route(cert_use, mode, BH, lists, counts, route_out, s);
   if (e != hipSuccess) return hip_fail(e, "route launch");
 
   // Each kernel's grid covers every head; slots past its list's count exit
@@ -171,21 +190,21 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
     f.mu = mu_use;
     f.head_list = lists;
     f.head_count = counts;
-    if ((e = launch_attn(f, dtype, true, s)) != hipSuccess) return hip_fail(e, "fixed attention launch");
+    if ((e = launch_attn(f, dtype, true, vt, s)) != hipSuccess) return hip_fail(e, "fixed attention launch");
   }
   if (mode != CLIS_MODE_FIXED) {
     clis::AttnArgs g = a;
     g.head_list = lists + BH;
     g.head_count = counts + 1;
-    if ((e = launch_attn(g, dtype, false, s)) != hipSuccess) return hip_fail(e, "online attention launch");
+    if ((e = launch_attn(g, dtype, false, vt, s)) != hipSuccess) return hip_fail(e, "online attention launch");
   }
   return CLIS_OK;
 }
 
 int online_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int Nq, int Nk,
-                    int d, float scale, int causal, int dtype, void* stream) {
+                    int d, float scale, int causal, int dtype, void* ws, size_t ws_bytes, void* stream) {
   return clis_attn_fwd(q, k, v, o, B, H, Nq, Nk, d, scale, causal, dtype, CLIS_MODE_ONLINE, nullptr,
-                       nullptr, nullptr, nullptr, 0, stream);
+                       nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 const char* clis_status_string(int status) {

@@ -115,6 +115,30 @@ __device__ __forceinline__ void load_kv_tile(const char* Kh, const char* Vh, int
   }
 }
 
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X).
+// CLIS_FIXED_PIPE: 0 = scores of both 32-key blocks, then weights, then both
+// products; 1 = block-pipelined order (block 1's scores and block 0's product
+// overlap the other block's weights); 2 = as 1 with explicit interleave hints.
+#ifndef CLIS_FIXED_PIPE
+#define CLIS_FIXED_PIPE 1
+#endif
+#ifndef CLIS_HINT_A
+#define CLIS_HINT_A 5
+#endif
+#ifndef CLIS_HINT_B
+#define CLIS_HINT_B 3
+#endif
+
+// Scheduling hints: ask the compiler to interleave `n` rounds of
+// {1 MFMA, v VALU} so the matrix core and the vector ALU work side by side.
+#define CLIS_INTERLEAVE(n, v)                                  \
+  do {                                                         \
+    _Pragma("unroll") for (int i_ = 0; i_ < (n); ++i_) {       \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       \
+      __builtin_amdgcn_sched_group_barrier(0x002, (v), 0);     \
+    }                                                          \
+  } while (0)
+
 template <int D, bool FIXED, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -195,62 +219,120 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  auto tile = [&](int it, auto stage_tag) {
+  // S^T for one 32-key block of the tile (8 MFMAs at d=128)
+  auto qk = [&](const char* Ks, int kb) {
+    floatx16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      acc = mfma32(*reinterpret_cast<const bf16x8*>(Ks + kb * 32 * D * 2 + kro[s]), qf[s], acc);
+    return acc;
+  };
+  // Register r of block kb holds key kt + 32 kb + 8 (r / 4) + 4 g + r % 4.
+  auto visible = [&](int kt, int kb, int r) {
+    const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+    return key < Nk && (!CAUSAL || key <= qrow);
+  };
+  // bf16 weights of one block, packed for the PV product, and their row sum
+  auto pack_block = [&](const float* p, uint32_t* pw) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pw[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), ones, lsum, false);
+    }
+  };
+  // O^T += V^T P^T for one block: k-step t covers registers 8t..8t+7, i.e.
+  // keys 32 kb + 16 t + {4g..4g+3, 8+4g..8+4g+3}
+  auto pv = [&](const char* Vs, int kb, const uint32_t* pw) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[4 * t], pw[4 * t + 1], pw[4 * t + 2], pw[4 * t + 3]));
+      const int rbase = (kb * 32 + 16 * t) * D * 2;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(Vs + rbase + vro[c]));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(Vs + rbase + 8 * D * 2 + vro[c]));
+        const short4v both[2] = {lo, hi};
+        oacc[c] = mfma32(__builtin_bit_cast(bf16x8, both), pf, oacc[c]);
+      }
+    }
+  };
+
+  auto tile = [&](int it, auto stage_tag, auto mask_tag, bool need_mask) {
     constexpr int ST = decltype(stage_tag)::value;
+    constexpr bool MASK = decltype(mask_tag)::value;
+    (void)need_mask;
     const int kt = it * kBN;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile `it` is in LDS; nobody still reads the other stage
-    if (it + 1 < ntiles) load_tile(kt + kBN, ST ^ 1);
-    if (CAUSAL && kt > row0 + 31) return;  // every key of the tile is above this wave's rows
     const char* Ks = lds + ST * G::STAGE_BYTES;
     const char* Vs = Ks + G::TILE_BYTES;
-
-    // ---- S^T = K Q^T for two 32-key blocks
-    floatx16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {  // the two blocks' chains alternate
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(Ks + kro[s]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(Ks + 32 * D * 2 + kro[s]);
-      sacc[0] = mfma32(a0, qf[s], sacc[0]);
-      sacc[1] = mfma32(a1, qf[s], sacc[1]);
-    }
-
-    // ---- exp2 weights.  Register r of block kb holds key
-    //      kt + 32 kb + 8 (r / 4) + 4 g + r % 4.
-    const bool need_mask = (kt + kBN > Nk) || (CAUSAL && kt + kBN - 1 > row0);
-    float p[2][16];
     if constexpr (FIXED) {
-      if (!need_mask) {
+      float p0[16], p1[16];
+      uint32_t pw0[8], pw1[8];
+      // no running maximum: x = c s - mu with mu fixed, weights 2^x
+      auto weights = [&](const floatx16& sacc, int kb, float* p) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int r = 0; r < 16; ++r) {
+          p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c2, negmu));
+          if constexpr (MASK) p[r] = visible(kt, kb, r) ? p[r] : 0.f;
+        }
+      };
+#if CLIS_FIXED_PIPE == 0
+      // both blocks' scores, then all weights, then both products
+      floatx16 sacc[2];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) p[kb][r] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, negmu));
-      } else {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool ok = key < Nk && (!CAUSAL || key <= qrow);
-            p[kb][r] = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, negmu)) : 0.f;
-          }
+      for (int s = 0; s < NS; ++s) {  // the two blocks' chains alternate
+        sacc[0] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + kro[s]), qf[s], sacc[0]);
+        sacc[1] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + 32 * D * 2 + kro[s]), qf[s], sacc[1]);
       }
+      weights(sacc[0], 0, p0);
+      weights(sacc[1], 1, p1);
+      pack_block(p0, pw0);
+      pv(Vs, 0, pw0);
+      pack_block(p1, pw1);
+      pv(Vs, 1, pw1);
+#else
+      const floatx16 s0 = qk(Ks, 0);
+      const floatx16 s1 = qk(Ks, 1);  // overlaps the weights of block 0
+      weights(s0, 0, p0);
+      pack_block(p0, pw0);
+#if CLIS_FIXED_PIPE == 2
+      CLIS_INTERLEAVE(NS, CLIS_HINT_A);
+#endif
+      pv(Vs, 0, pw0);                 // overlaps the weights of block 1
+      weights(s1, 1, p1);
+      pack_block(p1, pw1);
+#if CLIS_FIXED_PIPE == 2
+      CLIS_INTERLEAVE(2 * NC, CLIS_HINT_B);
+#endif
+      pv(Vs, 1, pw1);
+#endif
     } else {
+      // online softmax: the tile maximum must be known before any weight,
+      // and every weight waits for it
+      floatx16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {  // the two blocks' chains alternate
+        sacc[0] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + kro[s]), qf[s], sacc[0]);
+        sacc[1] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + 32 * D * 2 + kro[s]), qf[s], sacc[1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      float p[2][16];
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float x = sacc[kb][r] * c2;
-          if (need_mask) {
-            const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool ok = key < Nk && (!CAUSAL || key <= qrow);
-            x = ok ? x : -INFINITY;
-          }
+          if (need_mask) x = visible(kt, kb, r) ? x : -INFINITY;
           p[kb][r] = x;
           tmax = fmaxf(tmax, x);
         }
@@ -269,36 +351,51 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[c][r] *= alpha;
       mrow = mnew;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          uint32_t pw[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pw[e] = pack_bf16(p[kb][8 * t + 2 * e], p[kb][8 * t + 2 * e + 1]);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), ones, lsum, false);
+          }
+          const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+          const int rbase = (kb * 32 + 16 * t) * D * 2;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(Vs + rbase + vro[c]));
+            const short4v hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(Vs + rbase + 8 * D * 2 + vro[c]));
+            const short4v both[2] = {lo, hi};
+            oacc[c] = mfma32(__builtin_bit_cast(bf16x8, both), pf, oacc[c]);
+          }
+        }
     }
+  };
 
-    // ---- O^T += V^T P^T.  k-step t of block kb covers registers 8t..8t+7,
-    //      i.e. keys 32 kb + 16 t + {4g..4g+3, 8+4g..8+4g+3}.  The row sum
-    //      adds the same bf16-rounded weights that enter the product.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        uint32_t pw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pw[e] = pack_bf16(p[kb][8 * t + 2 * e], p[kb][8 * t + 2 * e + 1]);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), ones, lsum, false);
-        }
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-        const int rbase = (kb * 32 + 16 * t) * D * 2;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(Vs + rbase + vro[c]));
-          const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(Vs + rbase + 8 * D * 2 + vro[c]));
-          const short4v both[2] = {lo, hi};
-          oacc[c] = mfma32(__builtin_bit_cast(bf16x8, both), pf, oacc[c]);
-        }
-      }
+  auto step = [&](int it, auto stage_tag) {
+    constexpr int ST = decltype(stage_tag)::value;
+    const int kt = it * kBN;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile `it` is in LDS; nobody still reads the other stage
+    if (it + 1 < ntiles) load_tile(kt + kBN, ST ^ 1);
+    if (CAUSAL && kt > row0 + 31) return;  // every key of the tile is above this wave's rows
+    const bool need_mask = (kt + kBN > Nk) || (CAUSAL && kt + kBN - 1 > row0);
+    if constexpr (FIXED) {
+      // one straight-line body per mask case, so the scheduler can interleave
+      if (need_mask) tile(it, stage_tag, std::true_type{}, true);
+      else tile(it, stage_tag, std::false_type{}, false);
+    } else {
+      tile(it, stage_tag, std::false_type{}, need_mask);
+    }
   };
 
   for (int it = 0; it < ntiles; it += 2) {
-    tile(it, std::integral_constant<int, 0>{});
-    if (it + 1 < ntiles) tile(it + 1, std::integral_constant<int, 1>{});
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: the row sum's two halves meet, then O = O_acc / l

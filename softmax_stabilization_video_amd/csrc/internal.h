@@ -36,8 +36,12 @@ struct WsLayout {
   size_t cert;       // [BH]        int32
   size_t lists;      // [2][BH]     int32  heads routed fixed / online
   size_t counts;     // [2]         int32
+  size_t vt;         // [BH][d][Nk_pad] bf16  V^T for the bf16 attention kernels
   size_t total;
 };
+
+// Keys of the V^T copy, padded to whole 64-key tiles.
+inline int vt_pad(int Nk) { return (Nk + 63) / 64 * 64; }
 
 inline WsLayout ws_layout(int B, int H, int Nq, int Nk, int d) {
   const size_t BH = (size_t)B * H, Sk = cert_splits(Nk), Sq = cert_splits(Nq);
@@ -53,6 +57,7 @@ inline WsLayout ws_layout(int B, int H, int Nq, int Nk, int d) {
   w.cert = o;      o = align256(o + BH * sizeof(int32_t));
   w.lists = o;     o = align256(o + 2 * BH * sizeof(int32_t));
   w.counts = o;    o = align256(o + 2 * sizeof(int32_t));
+  w.vt = o;        o = align256(o + BH * (size_t)d * vt_pad(Nk) * 2);
   w.total = o;
   return w;
 }
@@ -87,6 +92,11 @@ struct AttnArgs {
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, bool fixed, hipStream_t s);
+
+// 64-rows-per-wave bf16 kernels, which read V through a transposed copy.
+int vt_padded_keys(int Nk);
+hipError_t launch_transpose_v(const void* v, void* vt, int BH, int Nk, int d, hipStream_t s);
+hipError_t launch_attn_bf16_r64(const AttnArgs& a, bool fixed, const void* vt, hipStream_t s);
 hipError_t launch_attn_fp32(const AttnArgs& a, bool fixed, hipStream_t s);
 
 }  // namespace clis

@@ -93,7 +93,8 @@ def test_empty_batch_is_a_no_op(clis):
     for B, H, Nq in ((0, 4, 10), (2, 0, 10), (2, 4, 0)):
         assert clis.lib.clis_attn_fwd(None, None, None, None, B, H, Nq, 10, 128, 0.1, 0, 0, 0, None, None,
                                       None, None, 0, None) == 0
-        assert clis.lib.online_attn_fwd(None, None, None, None, B, H, Nq, 10, 128, 0.1, 0, 0, None) == 0
+        assert clis.lib.online_attn_fwd(None, None, None, None, B, H, Nq, 10, 128, 0.1, 0, 0, None, 0,
+                                        None) == 0
         assert clis.lib.clis_certify(None, None, None, B, H, Nq, 10, 128, 0.1, 0, None, None, None, None,
                                      None, 0, None) == 0
 
