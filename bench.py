@@ -31,8 +31,8 @@ if ROOT not in sys.path:
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 MFMA_FP32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix
 METRIC = "attn fwd TFLOP/s & %MFMA peak, N=75600 H=20 d=128 bf16; CLiS vs online speedup"
-DOMINANT_SOURCE = os.path.join(ROOT, "softmax_stabilization_video_amd", "csrc", "attn_bf16_r64.hip")
-DOMINANT_KERNEL = "attn_fwd_bf16_r64<128, true, false>"
+DOMINANT_SOURCE = os.path.join(ROOT, "softmax_stabilization_video_amd", "csrc", "attn_bf16.hip")
+DOMINANT_KERNEL = "attn_fwd_bf16<128, true, false, 8>"
 
 
 def log(*a):

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libclis.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "certify.hip", "attn_bf16.hip", "attn_bf16_r64.hip", "attn_fp32.hip"]
+SOURCES = ["api.hip", "certify.hip", "attn_bf16.hip", "attn_fp32.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -102,18 +102,13 @@ clis::AttnArgs attn_args(const void* q, const void* k, const void* v, void* o, i
   return a;
 }
 
-// bf16 attention: 64 query rows per wave over a transposed V copy (default),
-// or the 32-rows-per-wave kernel that reads V directly.
-#ifndef CLIS_ATTN_ROWS
-#define CLIS_ATTN_ROWS 64
-#endif
-
 hipError_t launch_attn(const clis::AttnArgs& a, int dtype, bool fixed, const void* vt, hipStream_t s) {
   if (dtype != CLIS_BF16) return clis::launch_attn_fp32(a, fixed, s);
-  return CLIS_ATTN_ROWS == 64 ? clis::launch_attn_bf16_r64(a, fixed, vt, s) : clis::launch_attn_bf16(a, fixed, s);
+  return clis::launch_attn_bf16(a, fixed, vt, s);
 }
 
-bool needs_vt(int dtype) { return dtype == CLIS_BF16 && CLIS_ATTN_ROWS == 64; }
+// The bf16 kernels read V through a transposed copy in the workspace.
+bool needs_vt(int dtype) { return dtype == CLIS_BF16; }
 
 }  // namespace
 

@@ -1,39 +1,46 @@
 // attn_bf16.hip -- fused attention forward on gfx950 bf16 MFMA, in two
 // variants from one template:
 //   FIXED  -- CLiS: each query row's stabilizer mu_i is fixed before the key
-//             loop, so the loop has no running maximum, no cross-lane
-//             reduction and no accumulator rescaling ("CLiS: Plug-and-Play
-//             Attention Acceleration for Video Diffusion on TPUs via
-//             Certified Stabilization", abstract and Figure 5(a));
+//             loop, so the loop has no running maximum, no cross-lane step
+//             and no accumulator rescaling ("CLiS: Plug-and-Play Attention
+//             Acceleration for Video Diffusion on TPUs via Certified
+//             Stabilization", abstract and Figure 5(a));
 //   ONLINE -- online softmax: per key tile a running row maximum and a
 //             rescale factor alpha for the row sum and the output accumulator
 //             (the baseline those pages compare against).
+// The two variants use independently tuned workgroup sizes (the pages tune
+// tiles per method too, Table 7 caption).
 //
-// Work decomposition.  A workgroup of kWaves waves owns kBM = 32*kWaves query
-// rows of one (batch, head); each wave owns 32 rows.  Key/value tiles of kBN
-// rows stream through a two-stage LDS ring: the tile after the current one is
-// loaded with buffer loads that write LDS directly (buffer_load_dwordx4 ...
-// lds) while the current one is consumed, with one barrier per tile.  Both products use
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation, oriented so that every
-// lane owns one query row:
-//   S^T = K Q^T   A = K rows read from LDS (ds_read_b128), B = Q fragments
-//                 held in registers for the whole loop; lane l holds the
-//                 scores of query l%32 for 16 of every 32 keys (the other 16
-//                 sit in lane l^32).
-//   O^T = V^T P^T A = V^T fragments read from the row-major V tile with the
-//                 LDS transpose read ds_read_b64_tr_b16, B = P taken straight
-//                 from the S^T accumulators (converted to bf16).
-// Per-row quantities (mu, m, l, alpha) are therefore per lane; a row needs a
-// cross-lane step only between lanes l and l^32 (the online max per tile, and
-// the final row sum).
+// Work decomposition.  A workgroup of WAVES waves owns 32*WAVES query rows of
+// one (batch, head); each wave owns 32 rows, and two waves share a SIMD.  K
+// and V^T tiles of 64 keys stream through a two-stage LDS ring, loaded with
+// buffer loads that write LDS directly (buffer_load_dwordx4 ... lds), one
+// barrier per tile.  Both products use v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation, oriented so that every lane owns one query row:
+//   S^T = K Q^T   A = K rows from LDS (ds_read_b128), B = Q fragments held in
+//                 registers for the whole loop; lane l holds the scores of
+//                 query l%32 for 16 of every 32 keys (register r of a 32-key
+//                 block: key 8(r/4) + 4g + r%4, g = l/32); the other 16 keys
+//                 sit in lane l^32.
+//   O^T = V^T P^T A = V^T fragments from LDS (one ds_read_b128 each), B = P
+//                 straight from the S^T accumulators, converted to bf16.
+// Per-row quantities (mu, m, l, alpha) are therefore per lane; a row meets
+// lane l^32 only for the online tile maximum and the final row sum.
+//
+// V^T.  The P.V operand needs, per lane, eight keys of one channel: keys
+// 4g..4g+3 and 8+4g..8+4g+3 of a 16-key step.  transpose_v writes V^T per
+// head as [d][Nk_pad] with each 16-key group stored as {0-3, 8-11, 4-7,
+// 12-15}, which makes those eight keys contiguous, so one ds_read_b128 fetches
+// an operand (instead of two LDS transpose reads from a row-major V tile; on
+// gfx950 the LDS read issue rate bounds a 32-row MFMA attention).  Nk_pad is a
+// multiple of 128; keys past Nk are zero.
 //
 // LDS layouts.  Tiles are row-major with 16-byte chunks XOR-swizzled per row,
-// so the K operand reads (16 rows x 16 bytes per 16 lanes) and the V
-// transpose reads (4 rows x 64 bytes per 32 lanes) hit distinct banks.  The
-// swizzle is applied when loading: lane i of a load-to-LDS instruction writes
-// LDS slot base+16i, so each lane fetches the global chunk that belongs there.
-// Rows past the last key read as zeros (the buffer descriptor's range check),
-// and their weights are masked to 0.
+// so the 16 lanes that read one chunk position of 16 rows hit distinct banks.
+// The swizzle is applied when loading: lane i of a load-to-LDS instruction
+// writes slot base+16i, so each lane fetches the global chunk that belongs
+// there.  K rows past the last key read as zeros (the buffer descriptor's
+// range check) and their weights are masked to 0.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -42,20 +49,23 @@
 #include "internal.h"
 
 namespace clis {
-
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) short4v lds_short4;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;  // query rows per workgroup
-constexpr int kBN = 64;           // keys per tile
-constexpr int kXcds = 8;          // MI355X: workgroups are dealt round-robin to 8 XCDs
+// Waves per workgroup of each variant (measured best on MI355X).
+#ifndef CLIS_FIXED_WAVES
+#define CLIS_FIXED_WAVES 8
+#endif
+#ifndef CLIS_ONLINE_WAVES
+#define CLIS_ONLINE_WAVES 4
+#endif
+
+constexpr int kBN = 64;                   // keys per tile
+constexpr int kXcds = 8;                  // MI355X: workgroups are dealt round-robin to 8 XCDs
 constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor word 3 (untyped 32-bit data)
 
 __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, const floatx16& c) {
@@ -63,16 +73,9 @@ __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, con
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 v = {(__bf16)lo, (__bf16)hi};  // round to nearest even
   return __builtin_bit_cast(uint32_t, v);
 }
-
-// Per-row 16-byte chunk swizzles (see the file comment).
-template <int D>
-__device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
-template <int D>
-__device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
 // Logical block id for physical id `bid` when the first `active` blocks are
 // live: each XCD gets one contiguous range of logical ids, so the query tiles
@@ -83,73 +86,58 @@ __device__ __forceinline__ int xcd_remap(int bid, int active) {
   return (x < rem) ? x * (base + 1) + i : rem * (base + 1) + (x - rem) * base + i;
 }
 
-template <int D>
-struct Geometry {
-  static constexpr int NS = D / 16;                      // k-steps of the S product
-  static constexpr int NC = D / 32;                      // 32-channel output blocks
-  static constexpr int CPR = D / 8;                      // 16-byte chunks per tile row
-  static constexpr int TILE_BYTES = kBN * D * 2;         // one K or V tile
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;     // K then V
-  static constexpr int LOADS = kBN * CPR / kThreads;     // direct loads per lane per tile
+// Position of key k within its 16-key group in V^T: swap bits 2 and 3.
+__device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+template <int D, int WAVES>
+struct Geo {
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BM = 32 * WAVES;                 // query rows per workgroup
+  static constexpr int NS = D / 16;                     // k-steps of the S product
+  static constexpr int NC = D / 32;                     // 32-channel output blocks
+  static constexpr int KCPR = D / 8;                    // 16-byte chunks per K tile row (a key)
+  static constexpr int VCPR = kBN / 8;                  // 16-byte chunks per V^T tile row (a channel)
+  static constexpr int TILE_BYTES = kBN * D * 2;        // one K or V^T tile
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // K then V^T
+  static constexpr int LOADS = kBN * D / 8 / THREADS;   // 16-byte loads per lane per tile per tensor
 };
 
-// One wave's share of the K and V tiles starting at key kt: buffer loads that
-// write LDS directly (lane i -> slot base+16i).  The descriptors cover only
-// the rows that exist, so lanes past the last key read zeros without touching
-// memory.  gk/gv are the lanes' swizzled source offsets within a tile.
+// K tile row = one key (2D bytes): chunk swizzle for conflict-free 16-row reads.
 template <int D>
-__device__ __forceinline__ void load_kv_tile(const char* Kh, const char* Vh, int kt, int Nk, char* stage,
-                                             int wave, const uint32_t* gk, const uint32_t* gv) {
-  using G = Geometry<D>;
+__device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+// V^T tile row = one channel (128 bytes): two rows per 256 bytes of banks.
+__device__ __forceinline__ int swz_v(int row) { return (row >> 1) & 7; }
+
+// One wave's share of the K and V^T tiles at key kt (see the file comment).
+template <int D, int WAVES>
+__device__ __forceinline__ void load_tiles(const char* Kh, const char* Vth, int kt, int Nk, int vt_bytes,
+                                           char* stage, int wave, const uint32_t* gk, const uint32_t* gv) {
+  using G = Geo<D, WAVES>;
   char* kdst = stage + wave * 1024;
   char* vdst = kdst + G::TILE_BYTES;
-  const int bytes = min(Nk - kt, kBN) * D * 2;
+  const int kbytes = min(Nk - kt, kBN) * D * 2;
   const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Kh + (size_t)kt * D * 2), 0, bytes, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Kh + (size_t)kt * D * 2), 0, kbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Vh + (size_t)kt * D * 2), 0, bytes, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Vth + (size_t)kt * 2), 0, vt_bytes, kBufferFlags);
 #pragma unroll
   for (int j = 0; j < G::LOADS; ++j) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kdst + j * kThreads * 16), 16, gk[j], 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + j * kThreads * 16), 16, gv[j], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kdst + j * G::THREADS * 16), 16, gk[j], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + j * G::THREADS * 16), 16, gv[j], 0, 0, 0);
   }
 }
 
-// Tuning knobs (compile-time; the defaults are the measured best on MI355X).
-// CLIS_FIXED_PIPE: 0 = scores of both 32-key blocks, then weights, then both
-// products; 1 = block-pipelined order (block 1's scores and block 0's product
-// overlap the other block's weights); 2 = as 1 with explicit interleave hints.
-#ifndef CLIS_FIXED_PIPE
-#define CLIS_FIXED_PIPE 1
-#endif
-#ifndef CLIS_HINT_A
-#define CLIS_HINT_A 5
-#endif
-#ifndef CLIS_HINT_B
-#define CLIS_HINT_B 3
-#endif
-
-// Scheduling hints: ask the compiler to interleave `n` rounds of
-// {1 MFMA, v VALU} so the matrix core and the vector ALU work side by side.
-#define CLIS_INTERLEAVE(n, v)                                  \
-  do {                                                         \
-    _Pragma("unroll") for (int i_ = 0; i_ < (n); ++i_) {       \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       \
-      __builtin_amdgcn_sched_group_barrier(0x002, (v), 0);     \
-    }                                                          \
-  } while (0)
-
-template <int D, bool FIXED, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads, 2)
+template <int D, bool FIXED, bool CAUSAL, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2)
 attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-              const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+              const uint16_t* __restrict__ Vt, uint16_t* __restrict__ O,
               const float* __restrict__ mu, const int32_t* __restrict__ head_list,
-              const int32_t* __restrict__ head_count, int n_slots, int Nq, int Nk, float c2) {
-  using G = Geometry<D>;
-  constexpr int NS = G::NS, NC = G::NC;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * G::STAGE_BYTES];  // [stage][K tile, V tile]
+              const int32_t* __restrict__ head_count, int n_slots, int Nq, int Nk, int Nk_pad, float c2) {
+  using G = Geo<D, WAVES>;
+  constexpr int NS = G::NS, NC = G::NC, BM = G::BM;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * G::STAGE_BYTES];  // [stage][K tile, V^T tile]
 
-  const int n_qt = (Nq + kBM - 1) / kBM;
+  const int n_qt = (Nq + BM - 1) / BM;
   const int active = (head_list ? *head_count : n_slots) * n_qt;
   if ((int)blockIdx.x >= active) return;
   const int lid = xcd_remap(blockIdx.x, active);
@@ -161,44 +149,40 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, ln = lane & 31;
-  const int row0 = qt * kBM + wave * 32;  // first query row of this wave
+  const int row0 = qt * BM + wave * 32;  // first query row of this wave
   const int qrow = row0 + ln;
   const bool qvalid = qrow < Nq;
   const size_t qoff = ((size_t)bh * Nq + (qvalid ? qrow : 0)) * D;
   const char* Kh = reinterpret_cast<const char*>(K + (size_t)bh * Nk * D);
-  const char* Vh = reinterpret_cast<const char*>(V + (size_t)bh * Nk * D);
+  const char* Vth = reinterpret_cast<const char*>(Vt + (size_t)bh * D * Nk_pad);
+  const int vt_bytes = (D - 1) * Nk_pad * 2 + kBN * 2;  // one tile's span of V^T rows
 
-  const int kv_end = CAUSAL ? min(Nk, (qt + 1) * kBM) : Nk;
+  const int kv_end = CAUSAL ? min(Nk, (qt + 1) * BM) : Nk;
   const int ntiles = (kv_end + kBN - 1) / kBN;
 
   // ---- per-lane, loop-invariant offsets
-  // direct loads: lane slot -> (tile row, physical chunk) -> swizzled source chunk
-  uint32_t gk[G::LOADS], gv[G::LOADS];
+  uint32_t gk[G::LOADS], gv[G::LOADS];  // load-to-LDS sources within a tile
 #pragma unroll
   for (int j = 0; j < G::LOADS; ++j) {
-    const int s = (j * kWaves + wave) * 64 + lane;
-    const int row = s / G::CPR, p = s % G::CPR;
-    gk[j] = (uint32_t)(row * D + (p ^ swz_k<D>(row)) * 8) * 2;
-    gv[j] = (uint32_t)(row * D + (p ^ swz_v<D>(row)) * 8) * 2;
+    const int s = (j * WAVES + wave) * 64 + lane;
+    const int krow = s / G::KCPR, kp = s % G::KCPR;
+    gk[j] = (uint32_t)(krow * D + (kp ^ swz_k<D>(krow)) * 8) * 2;
+    const int vrow = s / G::VCPR, vp = s % G::VCPR;
+    gv[j] = (uint32_t)vrow * Nk_pad * 2 + (uint32_t)((vp ^ swz_v(vrow)) * 16);
   }
-  // K operand reads: row ln of a 32-key block, chunk 2s+g, swizzled
-  uint32_t kro[NS];
+  uint32_t kro[NS];  // K fragment: row ln of a 32-key block, chunk 2s+g
 #pragma unroll
   for (int s = 0; s < NS; ++s) kro[s] = (uint32_t)(ln * D + (((2 * s + g) ^ swz_k<D>(ln)) * 8)) * 2;
-  // V transpose reads: 16-lane group supplies 4 rows x 16 channels
-  const int tr_r = (lane & 15) >> 2, tr_q = lane & 3, tr_hc = (lane >> 4) & 1;
-  uint32_t vro[NC];
+  // V^T fragment of (32-key block kb, 16-key step t, channel block c): row
+  // 32c + ln, V^T positions 32kb + 16t + 8g .. +7, i.e. chunk 2(2kb + t) + g
+  uint32_t vro[4];
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-    vro[c] = (uint32_t)((4 * g + tr_r) * D + ((4 * c + 2 * tr_hc + (tr_q >> 1)) ^ swz_v<D>(tr_r)) * 8 +
-                        4 * (tr_q & 1)) * 2;
+  for (int q = 0; q < 4; ++q) vro[q] = (uint32_t)(ln * kBN * 2 + (((2 * q + g) ^ swz_v(ln)) * 16));
 
   auto load_tile = [&](int kt, int stage) {
-    load_kv_tile<D>(Kh, Vh, kt, Nk, lds + stage * G::STAGE_BYTES, wave, gk, gv);
+    load_tiles<D, WAVES>(Kh, Vth, kt, Nk, vt_bytes, lds + stage * G::STAGE_BYTES, wave, gk, gv);
   };
-
-  // first tile in flight before anything else
-  load_tile(0, 0);
+  load_tile(0, 0);  // first tile in flight before anything else
 
   bf16x8 qf[NS];
 #pragma unroll
@@ -216,10 +200,9 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[c][r] = 0.f;
 
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // S^T for one 32-key block of the tile (8 MFMAs at d=128)
+  // S^T of one 32-key block
   auto qk = [&](const char* Ks, int kb) {
     floatx16 acc;
 #pragma unroll
@@ -229,150 +212,95 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       acc = mfma32(*reinterpret_cast<const bf16x8*>(Ks + kb * 32 * D * 2 + kro[s]), qf[s], acc);
     return acc;
   };
-  // Register r of block kb holds key kt + 32 kb + 8 (r / 4) + 4 g + r % 4.
   auto visible = [&](int kt, int kb, int r) {
     const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
     return key < Nk && (!CAUSAL || key <= qrow);
   };
-  // bf16 weights of one block, packed for the PV product, and their row sum
-  auto pack_block = [&](const float* p, uint32_t* pw) {
+  // bf16 weights of one block packed for the product; the row sum adds the
+  // same rounded weights
+  auto pack = [&](const float* p, uint32_t* pw) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       pw[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
       lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), ones, lsum, false);
     }
   };
-  // O^T += V^T P^T for one block: k-step t covers registers 8t..8t+7, i.e.
-  // keys 32 kb + 16 t + {4g..4g+3, 8+4g..8+4g+3}
+  // O^T += V^T P^T for one 32-key block
   auto pv = [&](const char* Vs, int kb, const uint32_t* pw) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[4 * t], pw[4 * t + 1], pw[4 * t + 2], pw[4 * t + 3]));
-      const int rbase = (kb * 32 + 16 * t) * D * 2;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(Vs + rbase + vro[c]));
-        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(Vs + rbase + 8 * D * 2 + vro[c]));
-        const short4v both[2] = {lo, hi};
-        oacc[c] = mfma32(__builtin_bit_cast(bf16x8, both), pf, oacc[c]);
-      }
+      for (int c = 0; c < NC; ++c)
+        oacc[c] = mfma32(*reinterpret_cast<const bf16x8*>(Vs + c * 32 * kBN * 2 + vro[2 * kb + t]), pf, oacc[c]);
     }
   };
 
   auto tile = [&](int it, auto stage_tag, auto mask_tag, bool need_mask) {
     constexpr int ST = decltype(stage_tag)::value;
     constexpr bool MASK = decltype(mask_tag)::value;
-    (void)need_mask;
     const int kt = it * kBN;
     const char* Ks = lds + ST * G::STAGE_BYTES;
     const char* Vs = Ks + G::TILE_BYTES;
     if constexpr (FIXED) {
-      float p0[16], p1[16];
-      uint32_t pw0[8], pw1[8];
       // no running maximum: x = c s - mu with mu fixed, weights 2^x
-      auto weights = [&](const floatx16& sacc, int kb, float* p) {
+      (void)need_mask;
+      auto weights = [&](const floatx16& sacc, int kb, uint32_t* pw) {
+        float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c2, negmu));
           if constexpr (MASK) p[r] = visible(kt, kb, r) ? p[r] : 0.f;
         }
+        pack(p, pw);
       };
-#if CLIS_FIXED_PIPE == 0
-      // both blocks' scores, then all weights, then both products
-      floatx16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {  // the two blocks' chains alternate
-        sacc[0] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + kro[s]), qf[s], sacc[0]);
-        sacc[1] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + 32 * D * 2 + kro[s]), qf[s], sacc[1]);
-      }
-      weights(sacc[0], 0, p0);
-      weights(sacc[1], 1, p1);
-      pack_block(p0, pw0);
-      pv(Vs, 0, pw0);
-      pack_block(p1, pw1);
-      pv(Vs, 1, pw1);
-#else
+      // (the score products follow the closure above in source order: the
+      // other order schedules into 256 VGPRs with spills on hipcc 7.2)
       const floatx16 s0 = qk(Ks, 0);
-      const floatx16 s1 = qk(Ks, 1);  // overlaps the weights of block 0
-      weights(s0, 0, p0);
-      pack_block(p0, pw0);
-#if CLIS_FIXED_PIPE == 2
-      CLIS_INTERLEAVE(NS, CLIS_HINT_A);
-#endif
-      pv(Vs, 0, pw0);                 // overlaps the weights of block 1
-      weights(s1, 1, p1);
-      pack_block(p1, pw1);
-#if CLIS_FIXED_PIPE == 2
-      CLIS_INTERLEAVE(2 * NC, CLIS_HINT_B);
-#endif
+      const floatx16 s1 = qk(Ks, 1);
+      uint32_t pw0[8], pw1[8];
+      weights(s0, 0, pw0);
+      weights(s1, 1, pw1);
+      pv(Vs, 0, pw0);
       pv(Vs, 1, pw1);
-#endif
     } else {
+      const floatx16 s0 = qk(Ks, 0);
+      const floatx16 s1 = qk(Ks, 1);
       // online softmax: the tile maximum must be known before any weight,
       // and every weight waits for it
-      floatx16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {  // the two blocks' chains alternate
-        sacc[0] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + kro[s]), qf[s], sacc[0]);
-        sacc[1] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + 32 * D * 2 + kro[s]), qf[s], sacc[1]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      float p[2][16];
+      float x[2][16];
       float tmax = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sacc[kb][r] * c2;
-          if (need_mask) x = visible(kt, kb, r) ? x : -INFINITY;
-          p[kb][r] = x;
-          tmax = fmaxf(tmax, x);
+      for (int r = 0; r < 16; ++r) {
+        x[0][r] = s0[r] * c2;
+        x[1][r] = s1[r] * c2;
+        if (need_mask) {
+          x[0][r] = visible(kt, 0, r) ? x[0][r] : -INFINITY;
+          x[1][r] = visible(kt, 1, r) ? x[1][r] : -INFINITY;
         }
+        tmax = fmaxf(tmax, fmaxf(x[0][r], x[1][r]));
+      }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
       const float mnew = fmaxf(mrow, tmax);
       const bool none = (mnew == -INFINITY);  // no visible key yet
       const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(mrow - mnew);
       const float msub = none ? 0.f : mnew;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[kb][r] = __builtin_amdgcn_exp2f(p[kb][r] - msub);
+      mrow = mnew;
       lsum *= alpha;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[c][r] *= alpha;
-      mrow = mnew;
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          uint32_t pw[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pw[e] = pack_bf16(p[kb][8 * t + 2 * e], p[kb][8 * t + 2 * e + 1]);
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), ones, lsum, false);
-          }
-          const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-          const int rbase = (kb * 32 + 16 * t) * D * 2;
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(Vs + rbase + vro[c]));
-            const short4v hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(Vs + rbase + 8 * D * 2 + vro[c]));
-            const short4v both[2] = {lo, hi};
-            oacc[c] = mfma32(__builtin_bit_cast(bf16x8, both), pf, oacc[c]);
-          }
-        }
+      for (int r = 0; r < 16; ++r) {
+        x[0][r] = __builtin_amdgcn_exp2f(x[0][r] - msub);
+        x[1][r] = __builtin_amdgcn_exp2f(x[1][r] - msub);
+      }
+      uint32_t pw0[8], pw1[8];
+      pack(x[0], pw0);
+      pack(x[1], pw1);
+      pv(Vs, 0, pw0);
+      pv(Vs, 1, pw1);
     }
   };
 
@@ -385,7 +313,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (CAUSAL && kt > row0 + 31) return;  // every key of the tile is above this wave's rows
     const bool need_mask = (kt + kBN > Nk) || (CAUSAL && kt + kBN - 1 > row0);
     if constexpr (FIXED) {
-      // one straight-line body per mask case, so the scheduler can interleave
+      // one straight-line body per mask case
       if (need_mask) tile(it, stage_tag, std::true_type{}, true);
       else tile(it, stage_tag, std::false_type{}, false);
     } else {
@@ -415,29 +343,75 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
+// V [BH][Nk][D] -> V^T [BH][D][Nk_pad], keys permuted within 16-key groups
+// (vt_pos), zeros past the last key.  One block transposes 64 keys x D
+// channels through LDS: coalesced 16-byte reads along channels, coalesced
+// 16-byte writes along keys.
+template <int D>
+__global__ void __launch_bounds__(256)
+transpose_v(const uint16_t* __restrict__ V, uint16_t* __restrict__ Vt, int Nk, int Nk_pad) {
+  constexpr int TK = 64;               // keys per block
+  __shared__ uint16_t t[D][TK + 2];    // [channel][key position]; +2 breaks bank strides
+  const int bh = blockIdx.y, kt = blockIdx.x * TK;
+  const uint16_t* src = V + (size_t)bh * Nk * D;
+  uint16_t* dst = Vt + (size_t)bh * D * Nk_pad;
+  constexpr int CPR = D / 8;
+  for (int i = threadIdx.x; i < TK * CPR; i += 256) {
+    const int r = i / CPR, ch = i % CPR, key = kt + r;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (key < Nk) u = *reinterpret_cast<const uint4*>(src + (size_t)key * D + ch * 8);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const int pos = vt_pos(r);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      t[ch * 8 + 2 * e][pos] = (uint16_t)(w[e] & 0xffffu);
+      t[ch * 8 + 2 * e + 1][pos] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < D * (TK / 8); i += 256) {
+    const int c = i / (TK / 8), q = i % (TK / 8);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)t[c][q * 8 + 2 * e] | ((uint32_t)t[c][q * 8 + 2 * e + 1] << 16);
+    *reinterpret_cast<uint4*>(dst + (size_t)c * Nk_pad + kt + q * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 template <int D, bool FIXED, bool CAUSAL>
-hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
-  const int n_qt = (a.Nq + kBM - 1) / kBM;
+hipError_t launch_t(const AttnArgs& a, const uint16_t* vt, int nk_pad, hipStream_t s) {
+  constexpr int WAVES = FIXED ? CLIS_FIXED_WAVES : CLIS_ONLINE_WAVES;
+  using G = Geo<D, WAVES>;
+  const int n_qt = (a.Nq + G::BM - 1) / G::BM;
   const long long blocks = (long long)n_qt * a.n_slots;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  attn_fwd_bf16<D, FIXED, CAUSAL><<<(unsigned)blocks, kThreads, 0, s>>>(
-      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.mu, a.head_list,
-      a.head_count, a.n_slots, a.Nq, a.Nk, a.c2);
+  attn_fwd_bf16<D, FIXED, CAUSAL, WAVES><<<(unsigned)blocks, G::THREADS, 0, s>>>(
+      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), vt, static_cast<uint16_t*>(a.o),
+      a.mu, a.head_list, a.head_count, a.n_slots, a.Nq, a.Nk, nk_pad, a.c2);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const AttnArgs& a, bool fixed, hipStream_t s) {
-  if (fixed) return a.causal ? launch_t<D, true, true>(a, s) : launch_t<D, true, false>(a, s);
-  return a.causal ? launch_t<D, false, true>(a, s) : launch_t<D, false, false>(a, s);
+hipError_t launch_d(const AttnArgs& a, bool fixed, const uint16_t* vt, int nk_pad, hipStream_t s) {
+  if (fixed) return a.causal ? launch_t<D, true, true>(a, vt, nk_pad, s) : launch_t<D, true, false>(a, vt, nk_pad, s);
+  return a.causal ? launch_t<D, false, true>(a, vt, nk_pad, s) : launch_t<D, false, false>(a, vt, nk_pad, s);
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnArgs& a, bool fixed, hipStream_t s) {
-  if (a.d == 128) return launch_d<128>(a, fixed, s);
-  if (a.d == 64) return launch_d<64>(a, fixed, s);
+hipError_t launch_transpose_v(const void* v, void* vt, int BH, int Nk, int d, hipStream_t s) {
+  const dim3 grid((unsigned)(vt_pad(Nk) / 64), (unsigned)BH);
+  if (d == 128) transpose_v<128><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), static_cast<uint16_t*>(vt), Nk, vt_pad(Nk));
+  else if (d == 64) transpose_v<64><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), static_cast<uint16_t*>(vt), Nk, vt_pad(Nk));
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, bool fixed, const void* vt, hipStream_t s) {
+  const int nk_pad = vt_pad(a.Nk);
+  const uint16_t* v = static_cast<const uint16_t*>(vt);
+  if (a.d == 128) return launch_d<128>(a, fixed, v, nk_pad, s);
+  if (a.d == 64) return launch_d<64>(a, fixed, v, nk_pad, s);
   return hipErrorInvalidValue;
 }
 

@@ -40,8 +40,8 @@ struct WsLayout {
   size_t total;
 };
 
-// Keys of the V^T copy, padded to whole 64-key tiles.
-inline int vt_pad(int Nk) { return (Nk + 63) / 64 * 64; }
+// Keys of the V^T copy, padded to whole 128-key tiles (either tile size).
+inline int vt_pad(int Nk) { return (Nk + 127) / 128 * 128; }
 
 inline WsLayout ws_layout(int B, int H, int Nq, int Nk, int d) {
   const size_t BH = (size_t)B * H, Sk = cert_splits(Nk), Sq = cert_splits(Nq);
@@ -91,12 +91,10 @@ struct AttnArgs {
   int causal;
 };
 
-hipError_t launch_attn_bf16(const AttnArgs& a, bool fixed, hipStream_t s);
-
-// 64-rows-per-wave bf16 kernels, which read V through a transposed copy.
-int vt_padded_keys(int Nk);
+// bf16 kernels: V is read through a transposed copy [BH][d][vt_pad(Nk)]
+// that launch_transpose_v writes.
 hipError_t launch_transpose_v(const void* v, void* vt, int BH, int Nk, int d, hipStream_t s);
-hipError_t launch_attn_bf16_r64(const AttnArgs& a, bool fixed, const void* vt, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, bool fixed, const void* vt, hipStream_t s);
 hipError_t launch_attn_fp32(const AttnArgs& a, bool fixed, hipStream_t s);
 
 }  // namespace clis
