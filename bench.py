@@ -11,8 +11,11 @@ shape at one GPU's share of heads (B=1, H=20, N=75,600, d=128, bf16).
 Printed: ONE JSON line with the step throughput (attention TFLOP/s), the
 CLiS kernel alone, the online-softmax baseline, their speedup, the roofline
 of the dominant kernel (the fixed-stabilizer attention kernel; per-launch
-durations from HIP events on the stream the library launches on) and the
-fp64 CPU oracle timed on a bounded sample of the same workload.
+durations from HIP events on the stream the library launches on), the rate
+of an MFMA-only probe on the same GPU, the fp64 CPU oracle timed on a
+bounded sample of the same workload, and the step's output checked against
+that oracle sample (and every head's certification flag against the
+oracle's).
 """
 from __future__ import annotations
 
@@ -29,10 +32,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
-MFMA_FP32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
 METRIC = "attn fwd TFLOP/s & %MFMA peak, N=75600 H=20 d=128 bf16; CLiS vs online speedup"
-DOMINANT_SOURCE = os.path.join(ROOT, "softmax_stabilization_video_amd", "csrc", "attn_bf16.hip")
-DOMINANT_KERNEL = "attn_fwd_bf16<128, true, false, 8>"
+CSRC = os.path.join(ROOT, "softmax_stabilization_video_amd", "csrc")
+
+
+def dominant_kernel(w):
+    """(name, source) of the fixed-stabilizer kernel that runs this workload."""
+    c = "true" if w.causal else "false"
+    if w.dtype == "bf16":
+        return f"attn_fwd_bf16<{w.d}, true, {c}, 8>", os.path.join(CSRC, "attn_bf16.hip")
+    return f"attn_fwd_fp32<{w.d}, true, {c}>", os.path.join(CSRC, "attn_fp32.hip")
 
 
 def log(*a):
@@ -55,7 +65,7 @@ def time_calls(fn, n: int, stream) -> list:
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, source: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -65,32 +75,54 @@ def measured_traffic(kernel: str, workload: str):
         rec = json.load(open(path)).get(f"{kernel}/{workload}")
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha256_16") != source_hash(DOMINANT_SOURCE):
+    if not rec or rec.get("source_sha256_16") != source_hash(source):
         return None
     return rec.get("bytes_per_launch")
 
 
+def mfma_probe(device, iters: int = 40000, blocks: int = 2048, reps: int = 5):
+    """Rate (TFLOP/s) of an MFMA-only loop of the attention kernels' MFMA
+    (libclis_probe.so), about 25 ms per call: the sustained matrix-core rate
+    of this GPU, as a measured ceiling beside the published peak."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "softmax_stabilization_video_amd", "libclis_probe.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.clis_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.clis_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.clis_probe_mfma_flops.restype = ctypes.c_double
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        r = L.clis_probe_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters, ctypes.c_void_p(stream.cuda_stream))
+        if r != 0:
+            raise RuntimeError(f"clis_probe_mfma failed: {r}")
+    for _ in range(2):
+        call()
+    ms = statistics.median(time_calls(call, reps, stream))
+    return L.clis_probe_mfma_flops(blocks, iters) / (ms * 1e-3) / 1e12
+
+
 def cpu_baseline(w, Q, K, V, budget_s: float):
     """The fp64 oracle (as it stands) on a bounded sample of the workload:
-    softmax attention for a seeded set of query rows of every head."""
+    softmax attention for a seeded set of query rows of every head.  Returns
+    the record and the sample ({(b, h): (rows, oracle rows)})."""
     import numpy as np
     import oracle
-    import workloads
     threads = oracle.default_threads()
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    dec = {}
 
     def head_inputs(b, h):
-        if (b, h) not in dec:
-            dec[(b, h)] = tuple(oracle.decode(a[b, h], w.dtype) for a in (Q, K, V))
-        return dec[(b, h)]
+        return tuple(oracle.decode(a[b, h], w.dtype) for a in (Q, K, V))
 
     rng = np.random.default_rng(12345)
-    per_row = 4.0 * w.Nk * w.d if not w.causal else 2.0 * w.Nk * w.d  # mean over rows for causal
-    # calibrate on one small batch, then size the sample to the time budget
-    b0, h0 = heads[0]
-    q, k, v = head_inputs(b0, h0)
-    rows = np.sort(rng.choice(w.Nq, size=min(w.Nq, 2 * threads), replace=False))
+    # calibrate on one batch of rows, then size the sample to the time budget
+    q, k, v = head_inputs(*heads[0])
+    rows = np.sort(rng.choice(w.Nq, size=min(w.Nq, 8 * threads), replace=False))
+    oracle.attention_head(q, k, v, w.scale, w.causal, rows=rows[:threads], threads=threads)  # warm
     t0 = time.perf_counter()
     oracle.attention_head(q, k, v, w.scale, w.causal, rows=rows, threads=threads)
     dt = max(time.perf_counter() - t0, 1e-6)
@@ -98,28 +130,59 @@ def cpu_baseline(w, Q, K, V, budget_s: float):
     n_rows = int(max(len(heads), min(budget_s * rate_rows, w.B * w.H * w.Nq)))
     per_head = max(1, n_rows // len(heads))
     total_rows, flops, t_total = 0, 0.0, 0.0
+    sample = {}
     for b, h in heads:
         q, k, v = head_inputs(b, h)
         rows = np.sort(rng.choice(w.Nq, size=min(w.Nq, per_head), replace=False))
         t0 = time.perf_counter()
-        oracle.attention_head(q, k, v, w.scale, w.causal, rows=rows, threads=threads)
+        ref = oracle.attention_head(q, k, v, w.scale, w.causal, rows=rows, threads=threads)
         t_total += time.perf_counter() - t0
+        sample[(b, h)] = (rows, ref)
         total_rows += len(rows)
         flops += float(np.sum([4.0 * w.d * ((r + 1) if w.causal else w.Nk) for r in rows]))
-        dec.pop((b, h), None)
     # certification of one head, timed the same way
     q, k, v = head_inputs(*heads[0])
     t0 = time.perf_counter()
     oracle.certify_head(q, k, v, w.scale, p_bf16=(w.dtype == "bf16"))
     t_cert = time.perf_counter() - t0
     full_s = t_total * (w.B * w.H * w.Nq) / total_rows + t_cert * len(heads)
-    return {
+    rec = {
         "value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": f"fp64 softmax attention of {total_rows} seeded query rows ({per_head} per head, all "
                   f"{len(heads)} heads) against all {w.Nk} keys; certification of 1 head timed separately",
         "sample_seconds": round(t_total, 3), "certify_one_head_s": round(t_cert, 3),
         "extrapolated_full_call_s": round(full_s, 1),
     }
+    return rec, sample
+
+
+def parity(w, Q, K, V, o_step, cert, sample):
+    """The step's output on the oracle sample's rows against the oracle, and
+    every head's certification flag against the oracle's (fp64 on both
+    sides, so the flags must be identical)."""
+    import numpy as np
+    import torch
+    import oracle
+    err_max, err_sum, n, num, den = 0.0, 0.0, 0, 0.0, 0.0
+    for (b, h), (rows, ref) in sample.items():
+        idx = torch.as_tensor(rows, dtype=torch.long, device=o_step.device)
+        got = o_step[b, h].index_select(0, idx).float().cpu().numpy().astype(np.float64)
+        e = np.abs(got - ref)
+        err_max = max(err_max, float(e.max()))
+        err_sum += float(e.sum())
+        n += e.size
+        num += float(np.sum((got - ref) ** 2))
+        den += float(np.sum(ref ** 2))
+    cert_gpu = cert.cpu().numpy()
+    agree = 0
+    for b in range(w.B):
+        for h in range(w.H):
+            q, k, v = (oracle.decode(a[b, h], w.dtype) for a in (Q, K, V))
+            c = oracle.certify_head(q, k, v, w.scale, p_bf16=(w.dtype == "bf16"))["cert"]
+            agree += int(int(c) == int(cert_gpu[b, h]))
+    return {"rows": sum(len(r) for r, _ in sample.values()), "max_abs": err_max, "mean_abs": err_sum / max(n, 1),
+            "rel_l2": (num / den) ** 0.5 if den > 0 else 0.0,
+            "flags_equal": f"{agree}/{w.B * w.H}", "vs": "fp64 oracle"}
 
 
 def main(argv=None):
@@ -129,7 +192,7 @@ def main(argv=None):
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="wan720p")
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    p.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", choices=["all", "clis", "online", "certify"], default="all",
                    help="restrict the extra timings (for profiler runs)")
@@ -177,6 +240,7 @@ def main(argv=None):
     ms_step = wall / args.steps * 1e3
     log(f"step (certify + attention): {ms_step:.3f} ms")
     step_events = time_calls(step, max(1, min(args.steps, args.reps)), stream)
+    o_step = o.clone()  # the step's output, checked against the oracle below
 
     mu, cert = clis.clis_certify(q, k, v, w.scale, workspace=ws)
     torch.cuda.synchronize()
@@ -231,20 +295,31 @@ def main(argv=None):
             out["kernel_speedup_vs_online"] = round(res["online_ms"] / res["clis_kernel_ms"], 4)
     if "certify_ms" in res:
         out["certify_ms"] = round(res["certify_ms"], 4)
-    if "fixed_kernel_ms_mean" in res and w.dtype == "bf16":
+    if "fixed_kernel_ms_mean" in res:
         ms = res["fixed_kernel_ms_mean"]
         achieved = flops / (ms * 1e-3) / 1e12
+        name, src = dominant_kernel(w)
+        bf16 = w.dtype == "bf16"
+        peak = MFMA_BF16_PEAK_TFLOPS if bf16 else FP32_VECTOR_PEAK_TFLOPS
         out["roofline"] = {
-            "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic(DOMINANT_KERNEL, w.name),
-            "kernel": DOMINANT_KERNEL + " (fixed stabilizer, dense; the timed call also runs the V "
-                      "transpose pre-pass and the route kernel)",
+            "bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(name, src, w.name),
+            "kernel": name + (" (fixed stabilizer; the timed call also runs the V transpose pre-pass and "
+                              "the route kernel)" if bf16 else " (fixed stabilizer; the timed call also runs "
+                              "the route kernel)"),
             "algorithmic_flops_per_launch": flops, "launch_ms_mean": round(ms, 4),
         }
+    if w.dtype == "bf16" and args.only == "all":
+        probe = mfma_probe(q.device)
+        if probe:
+            out["mfma_probe_tflops"] = round(probe, 1)
+            out["pct_measured_mfma_peak"] = round(100 * value / probe, 2)
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(w, Q, K, V, args.cpu_budget)
+        out["cpu_baseline"], sample = cpu_baseline(w, Q, K, V, args.cpu_budget)
+        log("checking the step's output and flags against the oracle")
+        out["parity"] = parity(w, Q, K, V, o_step, cert, sample)
     print(json.dumps(out), flush=True)
 
 

@@ -37,7 +37,7 @@
  * CLIS_OK is returned); a call with at least one query row needs Nk >= 1.
  * causal needs Nq == Nk (query i sees keys 0..i).  scale must be finite and
  * > 0.  Every dimension must fit in int32, B*H*N*d in int64, and one head's
- * keys must span less than 2 GiB (d * Nk * 2 bytes, Nk rounded up to 64).
+ * keys must span less than 2 GiB (d * Nk * 2 bytes, Nk rounded up to 128).
  */
 #ifndef CLIS_H
 #define CLIS_H

@@ -3,7 +3,9 @@
     python -m softmax_stabilization_video_amd.build
 
 Each .hip source is compiled to an object in parallel, then linked into a
-shared library next to this file.  Flags: gfx950 only; -O3; packed-fp32 VALU
+shared library next to this file.  A second, separate library,
+libclis_probe.so, holds the MFMA-rate probe that the benchmark reports
+beside the published peak.  Flags: gfx950 only; -O3; packed-fp32 VALU
 forms disabled (they are not used by this code and stay off by policy).
 """
 from __future__ import annotations
@@ -20,6 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libclis.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "certify.hip", "attn_bf16.hip", "attn_fp32.hip"]
+PROBE_SOURCES = ["probe_mfma.hip"]
+PROBE_LIB = os.path.join(HERE, "libclis_probe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -37,13 +41,11 @@ def _compile(src: str, extra=(), tag: str = "") -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
-    """Compile every source and link `out` (default: the package's libclis.so;
-    `extra` adds compiler flags, e.g. -D tuning knobs for a variant library)."""
+def _link(sources, extra, out: str) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    tag = "" if out == LIB else "." + os.path.basename(out).replace(".so", "")
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra, tag), SOURCES))
+    tag = "" if out in (LIB, PROBE_LIB) else "." + os.path.basename(out).replace(".so", "")
+    with ThreadPoolExecutor(len(sources)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra, tag), sources))
     tmp = out + f".tmp{os.getpid()}"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -55,10 +57,22 @@ def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
     missing = [l.strip() for l in nm.stdout.splitlines() if "clis::" in l]
     if missing:
         os.remove(tmp)
-        raise RuntimeError("libclis.so has undefined library symbols:\n" + "\n".join(missing))
+        raise RuntimeError(f"{os.path.basename(out)} has undefined library symbols:\n" + "\n".join(missing))
     os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
+    """Compile every source and link `out` (default: the package's libclis.so,
+    plus libclis_probe.so; `extra` adds compiler flags, e.g. -D tuning knobs
+    for a variant library, which skips the probe)."""
+    _link(SOURCES, extra, out)
     if verbose:
         print(f"built {out}")
+    if out == LIB:
+        _link(PROBE_SOURCES, (), PROBE_LIB)
+        if verbose:
+            print(f"built {PROBE_LIB}")
     return out
 
 
