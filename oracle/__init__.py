@@ -71,8 +71,10 @@ def _load(path):
     L.oracle_certify_head.argtypes = [dp, dp, dp, i64, i64, ci, cd, ci, dp, dp, ctypes.POINTER(CertRecord)]
     L.oracle_fixed_mu_rows.argtypes = [dp, dp, dp, i64, i64, ci, cd, ci, dp, ip, i64, dp, dp, dp]
     L.oracle_online_rows.argtypes = [dp, dp, dp, i64, i64, ci, cd, ci, i64, ip, i64, dp]
+    L.oracle_lse_rows.argtypes = [dp, dp, i64, i64, ci, cd, ci, ip, i64, dp]
+    L.oracle_fixed_mu_partial_rows.argtypes = [dp, dp, dp, i64, i64, ci, cd, ci, dp, i64, i64, ip, i64, dp, dp]
     for f in (L.oracle_attention_rows, L.oracle_certify_head, L.oracle_fixed_mu_rows,
-              L.oracle_online_rows):
+              L.oracle_online_rows, L.oracle_lse_rows, L.oracle_fixed_mu_partial_rows):
         f.restype = ctypes.c_int
     return L
 
@@ -227,6 +229,46 @@ def online_head(q, k, v, scale: float, causal: bool = False, block: int = 64, ro
 
     _fanout(run, rows, threads or default_threads())
     return out
+
+
+def lse_head(q, k, scale: float, causal: bool = False, rows=None, threads: int | None = None):
+    """Per-row log-sum-exp (natural log) of the scores scale * q_i . k_j over
+    the visible keys; [len(rows)] fp64."""
+    q, k = (np.ascontiguousarray(a, dtype=np.float64) for a in (q, k))
+    nq, d = q.shape
+    nk = k.shape[0]
+    rows = np.arange(nq, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.zeros(len(rows), dtype=np.float64)
+    L = lib()
+
+    def run(a, b):
+        L.oracle_lse_rows(_p(q), _p(k), nq, nk, d, float(scale), int(causal),
+                          _p(rows[a:b], ctypes.c_int64), b - a, _p(out[a:b]))
+
+    _fanout(run, rows, threads or default_threads())
+    return out
+
+
+def fixed_mu_partial_head(q, k, v, scale: float, mu, k0: int, k1: int, causal: bool = False, rows=None,
+                          threads: int | None = None):
+    """Unnormalized fixed-stabilizer sums over keys [k0, k1): (acc [rows, d],
+    l [rows]) with weights 2^(c q.k - mu), c = scale*log2(e)."""
+    q, k, v = (np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v))
+    mu = np.ascontiguousarray(mu, dtype=np.float64)
+    nq, d = q.shape
+    nk = k.shape[0]
+    rows = np.arange(nq, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    acc = np.zeros((len(rows), d), dtype=np.float64)
+    l = np.zeros(len(rows), dtype=np.float64)
+    L = lib()
+
+    def run(a, b):
+        L.oracle_fixed_mu_partial_rows(_p(q), _p(k), _p(v), nq, nk, d, float(scale), int(causal), _p(mu),
+                                       int(k0), int(k1), _p(rows[a:b], ctypes.c_int64), b - a,
+                                       _p(acc[a:b]), _p(l[a:b]))
+
+    _fanout(run, rows, threads or default_threads())
+    return acc, l
 
 
 # ---------------------------------------------------------------- batched

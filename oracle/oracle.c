@@ -23,7 +23,12 @@
  *    (the reading taken where the pages' Algorithm 1 extract stops);
  *  - two self-check evaluations of the same output: with the fixed stabilizer
  *    [CLiS Figure 5(a)], and with online softmax over key blocks
- *    [CLiS abstract: running maxima and accumulator rescaling].
+ *    [CLiS abstract: running maxima and accumulator rescaling];
+ *  - each row's log-sum-exp (natural log) of its scores, the statistic a
+ *    fused attention forward hands to its backward pass;
+ *  - the unnormalized fixed-stabilizer sums over a key range, whose values
+ *    over disjoint ranges add because the stabilizer does not change
+ *    [CLiS Figure 5(a)].
  */
 #include <float.h>
 #include <math.h>
@@ -299,5 +304,70 @@ int oracle_online_rows(const double* q, const double* k, const double* v,
     for (int c = 0; c < d; ++c) o[c] /= l;
   }
   free(s);
+  return 0;
+}
+
+/*
+ * Log-sum-exp of each listed row's scores, natural log:
+ *   lse_i = ln sum_j exp(s_j),  s_j = scale * q_i . k_j over the visible keys.
+ * Evaluated as m + ln sum_j exp(s_j - m), m the row maximum (the shift keeps
+ * fp64 in range; it does not change the value).  lse is [nrows].  Returns 0,
+ * or -1 on allocation failure.
+ */
+int oracle_lse_rows(const double* q, const double* k, int64_t nq, int64_t nk, int d, double scale,
+                    int causal, const int64_t* rows, int64_t nrows, double* lse) {
+  (void)nq;
+  double* s = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+  if (!s) return -1;
+  for (int64_t t = 0; t < nrows; ++t) {
+    const int64_t i = rows[t];
+    const int64_t n = visible_keys(i, nk, causal);
+    row_scores(q, k, i, n, d, scale, s);
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) m = s[j] > m ? s[j] : m;
+    double sum = 0.0;
+    for (int64_t j = 0; j < n; ++j) sum += exp(s[j] - m);
+    lse[t] = m + log(sum);
+  }
+  free(s);
+  return 0;
+}
+
+/*
+ * Unnormalized fixed-stabilizer sums of each listed row over the keys
+ * [k0, k1) that it sees [CLiS Figure 5(a): with mu_i fixed before the loop,
+ * the weights 2^{x_ij} of disjoint key ranges simply add]:
+ *   acc_i = sum_{j in [k0, k1), visible} 2^{x_ij} v_j,
+ *   l_i   = sum_{j in [k0, k1), visible} 2^{x_ij},
+ *   x_ij  = c (q_i . k_j) - mu_i,  c = scale * log2(e).
+ * k and v hold the whole head (key j is row j); acc is [nrows][d], l is
+ * [nrows]; an empty range gives zeros.  Returns 0.
+ */
+int oracle_fixed_mu_partial_rows(const double* q, const double* k, const double* v,
+                                 int64_t nq, int64_t nk, int d, double scale, int causal,
+                                 const double* mu, int64_t k0, int64_t k1,
+                                 const int64_t* rows, int64_t nrows, double* acc, double* l) {
+  (void)nq;
+  const double c2 = scale * LOG2E;
+  if (k0 < 0) k0 = 0;
+  for (int64_t t = 0; t < nrows; ++t) {
+    const int64_t i = rows[t];
+    const int64_t n = visible_keys(i, nk, causal);
+    const int64_t end = k1 < n ? k1 : n;
+    double* a = acc + t * (int64_t)d;
+    const double* qi = q + i * (int64_t)d;
+    double sum = 0.0;
+    for (int c = 0; c < d; ++c) a[c] = 0.0;
+    for (int64_t j = k0; j < end; ++j) {
+      const double* kj = k + j * (int64_t)d;
+      double dot = 0.0;
+      for (int c = 0; c < d; ++c) dot += qi[c] * kj[c];
+      const double p = exp2(c2 * dot - mu[i]);
+      sum += p;
+      const double* vj = v + j * (int64_t)d;
+      for (int c = 0; c < d; ++c) a[c] += p * vj[c];
+    }
+    l[t] = sum;
+  }
   return 0;
 }

@@ -8,7 +8,8 @@ certificate.  ``PINS`` lists them so that tests/test_oracle_mutations.py can
 plant mistakes in a copy of oracle.c and show that some pin catches each one.
 
 Pages: "CLiS: Plug-and-Play Attention Acceleration for Video Diffusion on
-TPUs via Certified Stabilization" -- abstract, Algorithm 1, Figure 3.
+TPUs via Certified Stabilization" -- abstract, Algorithm 1, Figure 3,
+Figure 5(a).
 """
 import math
 import os
@@ -277,9 +278,79 @@ def pin_certificate_is_safe():
     assert abs(mx[0] - rec["bound"]) < 1e-12 and abs(rec["bound"] - LOG2E * 2 * 5) < 1e-12
 
 
+# ------------------------------------------------------------ log-sum-exp
+def _brute_lse(q, k, i, scale, causal):
+    """Pure-Python ln sum_j exp(s_j) for one row, with no shift."""
+    n = i + 1 if causal else len(k)
+    return math.log(math.fsum(math.exp(scale * math.fsum(a * b for a, b in zip(q[i], k[j]))) for j in range(n)))
+
+
+def pin_lse():
+    rng = _rng(11)
+    for nq, nk, d, causal in [(1, 1, 1, False), (3, 5, 2, False), (4, 4, 3, True), (6, 2, 4, False),
+                              (5, 5, 1, True)]:
+        q, k = rng.standard_normal((nq, d)), rng.standard_normal((nk, d))
+        got = oracle.lse_head(q, k, 0.9, causal, threads=1)
+        want = [_brute_lse(q.tolist(), k.tolist(), i, 0.9, causal) for i in range(nq)]
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
+    # identical keys: lse_i = scale q_i.k + ln(number of visible keys)
+    q = rng.standard_normal((6, 3))
+    kk = np.tile(rng.standard_normal((1, 3)), (6, 1))
+    for causal in (False, True):
+        got = oracle.lse_head(q, kk, 0.5, causal, threads=1)
+        n = np.arange(1, 7) if causal else np.full(6, 6)
+        np.testing.assert_allclose(got, 0.5 * q @ kk[0] + np.log(n), rtol=0, atol=1e-13)
+    # scores far beyond exp's range: two keys at 1000, one at 0 -> 1000 + ln 2
+    got = oracle.lse_head(np.array([[1000.0]]), np.array([[1.0], [1.0], [0.0]]), 1.0, threads=1)
+    assert abs(got[0] - (1000.0 + math.log(2.0))) < 1e-12
+
+
+# ------------------------------------------------ fixed-mu partial sums
+def pin_partial_sums():
+    rng = _rng(12)
+    nq, nk, d, scale = 7, 11, 3, 0.8
+    q, k, v = (rng.standard_normal((n, d)) for n in (nq, nk, nk))
+    mu = rng.standard_normal(nq)
+    c2 = scale * LOG2E
+    # brute force: pure-Python weights 2^(c q.k - mu) over a key range
+    for k0, k1 in [(0, nk), (3, 8), (5, 5), (10, 11)]:
+        acc, l = oracle.fixed_mu_partial_head(q, k, v, scale, mu, k0, k1, threads=1)
+        for i in range(nq):
+            w = [2.0 ** (c2 * math.fsum(q[i, c] * k[j, c] for c in range(d)) - mu[i]) for j in range(k0, k1)]
+            assert abs(l[i] - math.fsum(w)) <= 1e-13 * max(1.0, abs(l[i]))
+            for c in range(d):
+                want = math.fsum(w[t] * v[k0 + t, c] for t in range(len(w)))
+                assert abs(acc[i, c] - want) <= 1e-12 * max(1.0, abs(want))
+    # disjoint ranges add; the full range normalizes to softmax attention
+    parts = [oracle.fixed_mu_partial_head(q, k, v, scale, mu, a, b, threads=1) for a, b in [(0, 4), (4, 9), (9, nk)]]
+    full_acc, full_l = oracle.fixed_mu_partial_head(q, k, v, scale, mu, 0, nk, threads=1)
+    np.testing.assert_allclose(sum(p[0] for p in parts), full_acc, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(sum(p[1] for p in parts), full_l, rtol=1e-12)
+    np.testing.assert_allclose(full_acc / full_l[:, None], oracle.attention_head(q, k, v, scale, threads=1),
+                               rtol=0, atol=1e-12)
+    # raising mu by an integer scales both sums by 2^-delta
+    acc3, l3 = oracle.fixed_mu_partial_head(q, k, v, scale, mu + 3.0, 0, nk, threads=1)
+    np.testing.assert_allclose(acc3, full_acc / 8.0, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(l3, full_l / 8.0, rtol=1e-13)
+    # causal: row i sees keys 0..i only
+    qc, kc, vc = (rng.standard_normal((6, d)) for _ in range(3))
+    mc = rng.standard_normal(6)
+    for i in range(6):
+        a_hi, l_hi = oracle.fixed_mu_partial_head(qc, kc, vc, scale, mc, i + 1, 6, causal=True, rows=[i], threads=1)
+        assert l_hi[0] == 0.0 and not a_hi.any()
+    a_c, l_c = oracle.fixed_mu_partial_head(qc, kc, vc, scale, mc, 0, 6, causal=True, threads=1)
+    np.testing.assert_allclose(a_c / l_c[:, None], oracle.attention_head(qc, kc, vc, scale, True, threads=1),
+                               rtol=0, atol=1e-12)
+    # with the certified mu, ln 2 (mu + log2 l) is the row's log-sum-exp
+    rec = oracle.certify_head(q, k, v, scale, p_bf16=False)
+    _, l_mu = oracle.fixed_mu_partial_head(q, k, v, scale, rec["mu"], 0, nk, threads=1)
+    np.testing.assert_allclose(math.log(2.0) * (rec["mu"] + np.log2(l_mu)), oracle.lse_head(q, k, scale, threads=1),
+                               rtol=0, atol=1e-13)
+
+
 PINS = [pin_brute_force, pin_closed_forms, pin_invariants, pin_weights_sum_to_one,
         pin_other_evaluations_agree, pin_cert_constants, pin_cert_closed_forms,
-        pin_cert_scaling_laws, pin_flag_flips, pin_certificate_is_safe]
+        pin_cert_scaling_laws, pin_flag_flips, pin_certificate_is_safe, pin_lse, pin_partial_sums]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)

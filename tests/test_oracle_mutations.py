@@ -39,6 +39,12 @@ MUTANTS = {
     "mu_sign": ("mu[r] = c2 * dot;", "mu[r] = -c2 * dot;"),
     "online_forgets_rescale": ("      l *= alpha;\n", "      l *= 1.0;\n"),
     "online_rescale_wrong_way": ("const double alpha = exp2(m - mn);", "const double alpha = exp2(mn - m);"),
+    "lse_log2_not_ln": ("lse[t] = m + log(sum);", "lse[t] = m + log2(sum);"),
+    "lse_drops_shift": ("for (int64_t j = 0; j < n; ++j) sum += exp(s[j] - m);",
+                        "for (int64_t j = 0; j < n; ++j) sum += exp(s[j]);"),
+    "partial_ignores_start": ("for (int64_t j = k0; j < end; ++j) {", "for (int64_t j = 0; j < end; ++j) {"),
+    "partial_ignores_causal": ("const int64_t end = k1 < n ? k1 : n;", "const int64_t end = k1 < nk ? k1 : nk;"),
+    "partial_mu_sign": ("const double p = exp2(c2 * dot - mu[i]);", "const double p = exp2(c2 * dot + mu[i]);"),
 }
 
 
