@@ -41,7 +41,7 @@ def dominant_kernel(w):
     """(name, source) of the fixed-stabilizer kernel that runs this workload."""
     c = "true" if w.causal else "false"
     if w.dtype == "bf16":
-        return f"attn_fwd_bf16<{w.d}, true, {c}, 8>", os.path.join(CSRC, "attn_bf16.hip")
+        return f"attn_fwd_bf16<{w.d}, true, {c}, 8, false>", os.path.join(CSRC, "attn_bf16.hip")
     return f"attn_fwd_fp32<{w.d}, true, {c}>", os.path.join(CSRC, "attn_fp32.hip")
 
 

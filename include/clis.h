@@ -35,7 +35,8 @@
  *
  * Shapes.  d must be 64 or 128.  B, H, Nq may be 0 (nothing is enqueued and
  * CLIS_OK is returned); a call with at least one query row needs Nk >= 1.
- * causal needs Nq == Nk (query i sees keys 0..i).  scale must be finite and
+ * causal needs Nq == Nk (query i sees keys 0..i), except for key shards
+ * (clis_attn_fwd_partial).  scale must be finite and
  * > 0.  Every dimension must fit in int32, B*H*N*d in int64, and one head's
  * keys must span less than 2 GiB (d * Nk * 2 bytes, Nk rounded up to 128).
  */
@@ -126,29 +127,75 @@ int clis_certify(const void* q, const void* k, const void* v,
  *              the mode needs them (auto: both, fixed: mu) and either is NULL,
  *              certification runs first inside this call, into ws.
  *   route_out  device [B, H] int32 (1 fixed, 0 online), or NULL.
+ *   lse_out    device [B, H, Nq] fp32, or NULL: each row's log-sum-exp
+ *              ln sum_j exp(scale * q_i . k_j) over its visible keys (natural
+ *              log), the statistic a backward pass of fused attention needs.
+ *              The fixed path gets it as ln 2 * (mu_i + log2 l_i) from its
+ *              row sum l_i, the online path as ln 2 * (m_i + log2 l_i) from its
+ *              final running maximum; no extra pass over the keys.
  *   ws         device workspace (clis_workspace_bytes()); may be NULL only if
  *              mode is online and dtype is fp32.
  * Output dtype equals input dtype: fp32 accumulation, bf16 stored with round
  * to nearest even; on the bf16 path the exp2 weights are rounded to bf16
- * (nearest even) before the P.V product.
+ * (nearest even) before the P.V product, and the row sums (hence lse) add the
+ * same rounded weights.
  */
 int clis_attn_fwd(const void* q, const void* k, const void* v, void* o,
                   int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
                   int mode, const float* mu, const int32_t* cert, int32_t* route_out,
-                  void* ws, size_t ws_bytes, void* stream);
+                  float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Online-softmax attention forward for every head: the tuned baseline and the
  * fallback path [CLiS abstract: running row maxima and accumulator
  * rescaling].  Per key tile: m' = max(m, tile max of c*s), alpha = 2^{m-m'},
  * l = alpha*l + sum 2^{c*s-m'}, O = alpha*O + P.V.  Bitwise equal to
- * clis_attn_fwd with CLIS_MODE_ONLINE.  The bf16 kernels read V through a
- * transposed copy kept in ws (clis_workspace_bytes()); ws may be NULL for
- * fp32.
+ * clis_attn_fwd with CLIS_MODE_ONLINE (lse_out as there, or NULL).  The bf16
+ * kernels read V through a transposed copy kept in ws (clis_workspace_bytes());
+ * ws may be NULL for fp32.
  */
 int online_attn_fwd(const void* q, const void* k, const void* v, void* o,
                     int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
-                    void* ws, size_t ws_bytes, void* stream);
+                    float* lse_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Key-sharded attention with a fixed stabilizer [CLiS Figure 5(a)]: with mu_i
+ * fixed for the whole key loop, the unnormalized sums of disjoint key ranges
+ *   o_acc_i = sum_j 2^{x_ij} v_j,   l_i = sum_j 2^{x_ij},
+ *   x_ij = scale*log2(e) * (q_i . k_j) - mu_i,
+ * simply add, with no max or rescale merge.  One call processes one shard of
+ * keys (k, v are [B, H, Nk, d] holding global keys kv_offset .. kv_offset+Nk-1)
+ * against all queries:
+ *   mu          device [B, H, Nq] fp32 stabilizers, required: from
+ *               clis_certify on the whole key set (a certified head's mu
+ *               keeps every shard's sums in range; an uncertified head may
+ *               overflow, as in CLIS_MODE_FIXED).
+ *   kv_offset   global index of this shard's first key, >= 0; only the
+ *               causal mask uses it (query i sees global keys 0..i; Nq need
+ *               not equal Nk here).
+ *   accumulate  0: overwrite o_acc and l_acc; 1: add this shard to them.
+ *   o_acc       device [B, H, Nq, d] fp32 (16-byte aligned), l_acc device
+ *               [B, H, Nq] fp32: unnormalized sums, caller-owned.
+ *   ws          device workspace of clis_workspace_bytes(B, H, Nq, Nk, d)
+ *               bytes (the shard's V^T); may be NULL for fp32.
+ * Shards may be any partition of the keys, in any order.  Finish with
+ * clis_attn_combine.
+ */
+int clis_attn_fwd_partial(const void* q, const void* k, const void* v,
+                          int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                          const float* mu, int kv_offset, int accumulate,
+                          float* o_acc, float* l_acc, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Finishes key-sharded attention: o = o_acc / l per row in the output dtype
+ * (bf16 round to nearest even, or fp32), and, if lse_out is set, each row's
+ * log-sum-exp ln 2 * (mu_i + log2 l_i) (mu then required).  o is
+ * [B, H, Nq, d], 16-byte aligned; a row whose l is 0 (it saw no key) gives
+ * Inf/NaN, as softmax over no keys is undefined.
+ */
+int clis_attn_combine(const float* o_acc, const float* l_acc, void* o,
+                      int B, int H, int Nq, int d, int dtype,
+                      const float* mu, float* lse_out, void* stream);
 
 /* Static text for a status code. */
 const char* clis_status_string(int status);
@@ -156,7 +203,7 @@ const char* clis_status_string(int status);
 /* Thread-local description of this thread's last failed call ("" if none). */
 const char* clis_last_error(void);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int clis_abi_version(void);
 
 #ifdef __cplusplus

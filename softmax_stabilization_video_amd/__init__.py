@@ -9,7 +9,9 @@ without a built library raises.
 Entry points (same names as the C ABI):
     clis_certify(q, k, v, scale)       -> (mu, cert[, stats, kbar])
     clis_attn_fwd(q, k, v, ...)        -> o            (mode auto/fixed/online)
-    online_attn_fwd(q, k, v, ...)      -> o
+    online_attn_fwd(q, k, v, ...)      -> o            (optionally with lse)
+    clis_attn_fwd_partial(q, k_shard, v_shard, mu, o_acc, l_acc, ...)
+    clis_attn_combine(o_acc, l_acc, ...) -> o        (optionally with lse)
 Tensors are [B, H, N, d], contiguous, bf16 or fp32, on the GPU.
 The library is loaded on first use; a missing build raises ImportError.
 
@@ -32,7 +34,8 @@ MODES = {"auto": 0, "fixed": 1, "online": 2}
 STATUS = {0: "CLIS_OK", 1: "CLIS_ERR_NULL", 2: "CLIS_ERR_SHAPE", 3: "CLIS_ERR_UNSUPPORTED",
           4: "CLIS_ERR_ALIGN", 5: "CLIS_ERR_WORKSPACE", 6: "CLIS_ERR_HIP"}
 EXPORTS = ["clis_workspace_bytes", "clis_certify", "clis_attn_fwd", "online_attn_fwd",
-           "clis_status_string", "clis_last_error", "clis_abi_version"]
+           "clis_attn_fwd_partial", "clis_attn_combine", "clis_status_string", "clis_last_error",
+           "clis_abi_version"]
 
 # clis_head_stats_t: 4 doubles, 6 int32
 STATS_DTYPE = np.dtype([("kappa", "<f8"), ("qnorm_max", "<f8"), ("bound", "<f8"), ("maxabs_v", "<f8"),
@@ -56,8 +59,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.clis_workspace_bytes.argtypes = [i, i, i, i, i]
     L.clis_workspace_bytes.restype = sz
     L.clis_certify.argtypes = [vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, vp, vp, sz, vp]
-    L.clis_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp, vp, vp, sz, vp]
-    L.online_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    L.clis_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+    L.online_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, vp, sz, vp]
+    L.clis_attn_fwd_partial.argtypes = [vp, vp, vp, i, i, i, i, i, f, i, i, vp, i, i, vp, vp, vp, sz, vp]
+    L.clis_attn_combine.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, vp]
     for fn in (L.clis_certify, L.clis_attn_fwd, L.online_attn_fwd, L.clis_abi_version):
         fn.restype = ctypes.c_int
     L.clis_status_string.argtypes = [i]
@@ -159,8 +164,11 @@ def decode_stats(stats) -> np.ndarray:
 
 
 def clis_attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, mode: str = "auto",
-                  mu=None, cert=None, out=None, want_route: bool = False, workspace=None, stream=None):
-    """CLiS attention forward (clis_attn_fwd).  Returns o, or (o, route)."""
+                  mu=None, cert=None, out=None, want_route: bool = False, want_lse: bool = False,
+                  workspace=None, stream=None):
+    """CLiS attention forward (clis_attn_fwd).  Returns o, plus route [B,H]
+    int32 and/or lse [B,H,Nq] fp32 when asked: o, (o, route), (o, lse) or
+    (o, route, lse)."""
     import torch
     B, H, Nq, Nk, d = _shapes(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -168,28 +176,72 @@ def clis_attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, mod
     if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
     route = torch.empty((B, H), dtype=torch.int32, device=q.device) if want_route else None
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if want_lse else None
     ws = workspace
     if ws is None and (mode != "online" or want_route or q.dtype != torch.float32):
         ws = new_workspace(B, H, Nq, Nk, d, q.device)
     _check(get_lib().clis_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Nq, Nk, d, scale, int(causal),
-                             _dtype_code(q), MODES[mode], _ptr(mu), _ptr(cert), _ptr(route), _ptr(ws),
-                             0 if ws is None else ws.numel(), _stream(stream)))
-    return (o, route) if want_route else o
+                             _dtype_code(q), MODES[mode], _ptr(mu), _ptr(cert), _ptr(route), _ptr(lse),
+                             _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    res = (o,) + ((route,) if want_route else ()) + ((lse,) if want_lse else ())
+    return res if len(res) > 1 else o
 
 
-def online_attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, workspace=None,
-                    stream=None):
-    """Online-softmax attention forward for every head (online_attn_fwd)."""
+def online_attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, want_lse: bool = False,
+                    workspace=None, stream=None):
+    """Online-softmax attention forward for every head (online_attn_fwd).
+    Returns o, or (o, lse)."""
     import torch
     B, H, Nq, Nk, d = _shapes(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if want_lse else None
     ws = workspace
     if ws is None and q.dtype != torch.float32:
         ws = new_workspace(B, H, Nq, Nk, d, q.device)
     _check(get_lib().online_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Nq, Nk, d, scale, int(causal),
-                                     _dtype_code(q), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
-    return o
+                                     _dtype_code(q), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
+                                     _stream(stream)))
+    return (o, lse) if want_lse else o
+
+
+def clis_attn_fwd_partial(q, k, v, mu, o_acc, l_acc, scale: float | None = None, causal: bool = False,
+                          kv_offset: int = 0, accumulate: bool = False, workspace=None, stream=None):
+    """One key shard of fixed-stabilizer attention (clis_attn_fwd_partial):
+    writes (accumulate=False) or adds to (True) the unnormalized fp32 sums
+    o_acc [B,H,Nq,d] and l_acc [B,H,Nq].  k, v hold global keys
+    kv_offset .. kv_offset + Nk - 1."""
+    import torch
+    B, H, Nq, Nk, d = _shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    for t, shape in ((o_acc, (B, H, Nq, d)), (l_acc, (B, H, Nq))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"accumulators must be contiguous fp32 of shape {shape}")
+    ws = workspace
+    if ws is None and q.dtype != torch.float32:
+        ws = new_workspace(B, H, Nq, Nk, d, q.device)
+    _check(get_lib().clis_attn_fwd_partial(_ptr(q), _ptr(k), _ptr(v), B, H, Nq, Nk, d, scale, int(causal),
+                                           _dtype_code(q), _ptr(mu), int(kv_offset), int(accumulate),
+                                           _ptr(o_acc), _ptr(l_acc), _ptr(ws), 0 if ws is None else ws.numel(),
+                                           _stream(stream)))
+    return o_acc, l_acc
+
+
+def clis_attn_combine(o_acc, l_acc, dtype=None, mu=None, want_lse: bool = False, out=None, stream=None):
+    """o = o_acc / l (clis_attn_combine) in `dtype` (default bf16); with
+    want_lse also each row's log-sum-exp ln 2 (mu + log2 l).  Returns o, or
+    (o, lse)."""
+    import torch
+    B, H, Nq, d = o_acc.shape
+    dtype = torch.bfloat16 if dtype is None else dtype
+    o = torch.empty((B, H, Nq, d), dtype=dtype, device=o_acc.device) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=o_acc.device) if want_lse else None
+    code = CLIS_BF16 if o.dtype == torch.bfloat16 else CLIS_FP32 if o.dtype == torch.float32 else None
+    if code is None:
+        raise ValueError("output dtype must be bf16 or fp32")
+    _check(get_lib().clis_attn_combine(_ptr(o_acc), _ptr(l_acc), _ptr(o), B, H, Nq, d, code, _ptr(mu), _ptr(lse),
+                                       _stream(stream)))
+    return (o, lse) if want_lse else o
 
 
 certify = clis_certify

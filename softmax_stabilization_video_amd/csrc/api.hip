@@ -135,7 +135,8 @@ int clis_certify(const void* q, const void* k, const void* v, int B, int H, int 
 
 int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int Nq, int Nk,
                   int d, float scale, int causal, int dtype, int mode, const float* mu,
-                  const int32_t* cert, int32_t* route_out, void* ws, size_t ws_bytes, void* stream) {
+                  const int32_t* cert, int32_t* route_out, float* lse_out, void* ws, size_t ws_bytes,
+                  void* stream) {
   g_err[0] = 0;
   if (mode != CLIS_MODE_AUTO && mode != CLIS_MODE_FIXED && mode != CLIS_MODE_ONLINE)
     return fail(CLIS_ERR_UNSUPPORTED, "unknown mode %d", mode);
@@ -143,8 +144,10 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
   int st = check_common(B, H, Nq, Nk, d, scale, dtype, causal, &empty);
   if (st != CLIS_OK || empty) return st;
   if ((st = check_io(q, k, v, o, true)) != CLIS_OK) return st;
+  if (lse_out && !aligned(lse_out, 4)) return fail(CLIS_ERR_ALIGN, "lse_out must be 4-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   clis::AttnArgs a = attn_args(q, k, v, o, B, H, Nq, Nk, d, scale, causal);
+  a.lse = lse_out;
   const bool plain_online = (mode == CLIS_MODE_ONLINE && !route_out);
   if (!plain_online || needs_vt(dtype)) {
     if ((st = check_ws(ws, ws_bytes, B, H, Nq, Nk, d)) != CLIS_OK) return st;
@@ -197,9 +200,62 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
 }
 
 int online_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int Nq, int Nk,
-                    int d, float scale, int causal, int dtype, void* ws, size_t ws_bytes, void* stream) {
+                    int d, float scale, int causal, int dtype, float* lse_out, void* ws, size_t ws_bytes,
+                    void* stream) {
   return clis_attn_fwd(q, k, v, o, B, H, Nq, Nk, d, scale, causal, dtype, CLIS_MODE_ONLINE, nullptr,
-                       nullptr, nullptr, ws, ws_bytes, stream);
+                       nullptr, nullptr, lse_out, ws, ws_bytes, stream);
+}
+
+int clis_attn_fwd_partial(const void* q, const void* k, const void* v, int B, int H, int Nq, int Nk, int d,
+                          float scale, int causal, int dtype, const float* mu, int kv_offset, int accumulate,
+                          float* o_acc, float* l_acc, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  bool empty = false;
+  // a causal shard need not be square: the mask compares global indices
+  int st = check_common(B, H, Nq, Nk, d, scale, dtype, 0, &empty);
+  if (st != CLIS_OK || empty) return st;
+  if ((st = check_io(q, k, v, nullptr, false)) != CLIS_OK) return st;
+  if (!mu || !o_acc || !l_acc) return fail(CLIS_ERR_NULL, "mu, o_acc and l_acc must be non-NULL");
+  if (!aligned(o_acc, 16) || !aligned(l_acc, 4) || !aligned(mu, 4))
+    return fail(CLIS_ERR_ALIGN, "o_acc must be 16-byte, l_acc and mu 4-byte aligned");
+  if (kv_offset < 0 || (long long)kv_offset + Nk > 0x7fffffffLL)
+    return fail(CLIS_ERR_SHAPE, "kv_offset %d out of range", kv_offset);
+  if (accumulate != 0 && accumulate != 1) return fail(CLIS_ERR_SHAPE, "accumulate must be 0 or 1");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  void* vt = nullptr;
+  if (needs_vt(dtype)) {
+    if ((st = check_ws(ws, ws_bytes, B, H, Nq, Nk, d)) != CLIS_OK) return st;
+    vt = at<void>(ws, clis::ws_layout(B, H, Nq, Nk, d).vt);
+    if ((e = clis::launch_transpose_v(v, vt, B * H, Nk, d, s)) != hipSuccess) return hip_fail(e, "V transpose launch");
+  }
+  clis::AttnArgs a = attn_args(q, k, v, nullptr, B, H, Nq, Nk, d, scale, causal);
+  a.mu = mu;
+  a.o_acc = o_acc;
+  a.l_acc = l_acc;
+  a.accumulate = accumulate;
+  a.kv_offset = kv_offset;
+  if ((e = launch_attn(a, dtype, true, vt, s)) != hipSuccess) return hip_fail(e, "key-shard attention launch");
+  return CLIS_OK;
+}
+
+int clis_attn_combine(const float* o_acc, const float* l_acc, void* o, int B, int H, int Nq, int d, int dtype,
+                      const float* mu, float* lse_out, void* stream) {
+  g_err[0] = 0;
+  if (B < 0 || H < 0 || Nq < 0) return fail(CLIS_ERR_SHAPE, "negative dimension (B=%d H=%d Nq=%d)", B, H, Nq);
+  if (dtype != CLIS_BF16 && dtype != CLIS_FP32) return fail(CLIS_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (d != 64 && d != 128) return fail(CLIS_ERR_UNSUPPORTED, "head dim %d not in {64, 128}", d);
+  const long long rows = (long long)B * H * Nq;
+  if (rows == 0) return CLIS_OK;
+  if (rows > (0x7fffffffffffffffLL / 4) / d) return fail(CLIS_ERR_SHAPE, "tensor too large");
+  if (!o_acc || !l_acc || !o) return fail(CLIS_ERR_NULL, "o_acc, l_acc and o must be non-NULL");
+  if (lse_out && !mu) return fail(CLIS_ERR_NULL, "lse_out needs mu");
+  if (!aligned(o_acc, 16) || !aligned(o, 16) || !aligned(l_acc, 4) || (lse_out && !aligned(lse_out, 4)) ||
+      (mu && !aligned(mu, 4)))
+    return fail(CLIS_ERR_ALIGN, "o_acc and o must be 16-byte, l_acc, mu and lse_out 4-byte aligned");
+  const hipError_t e = clis::launch_combine(o_acc, l_acc, o, dtype == CLIS_BF16, mu, lse_out, rows, d,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CLIS_OK : hip_fail(e, "combine launch");
 }
 
 const char* clis_status_string(int status) {
@@ -217,6 +273,6 @@ const char* clis_status_string(int status) {
 
 const char* clis_last_error(void) { return g_err; }
 
-int clis_abi_version(void) { return 1; }
+int clis_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -35,6 +35,14 @@
 // gfx950 the LDS read issue rate bounds a 32-row MFMA attention).  Nk_pad is a
 // multiple of 128; keys past Nk are zero.
 //
+// Outputs.  Normally O = O_acc / l in bf16, and optionally each row's
+// log-sum-exp ln 2 * (m + log2 l), where m is the fixed mu_i or the final
+// running maximum (both in log2 units).  With o_acc set (fixed variant only,
+// for key-value shards) the kernel instead starts from, or overwrites, fp32
+// unnormalized sums o_acc and l_acc: with a fixed stabilizer the sums over
+// disjoint key ranges simply add.  kv_offset is the global index of key 0
+// (the causal mask compares global key and query indices).
+//
 // LDS layouts.  Tiles are row-major with 16-byte chunks XOR-swizzled per row,
 // so the 16 lanes that read one chunk position of 16 rows hit distinct banks.
 // The swizzle is applied when loading: lane i of a load-to-LDS instruction
@@ -67,6 +75,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kBN = 64;                   // keys per tile
 constexpr int kXcds = 8;                  // MI355X: workgroups are dealt round-robin to 8 XCDs
 constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor word 3 (untyped 32-bit data)
+constexpr float kLn2 = 0.693147180559945309f;
 
 __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -127,13 +136,17 @@ __device__ __forceinline__ void load_tiles(const char* Kh, const char* Vth, int 
   }
 }
 
-template <int D, bool FIXED, bool CAUSAL, int WAVES>
+template <int D, bool FIXED, bool CAUSAL, int WAVES, bool PARTIAL>
 __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2)
 attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ Vt, uint16_t* __restrict__ O,
               const float* __restrict__ mu, const int32_t* __restrict__ head_list,
-              const int32_t* __restrict__ head_count, int n_slots, int Nq, int Nk, int Nk_pad, float c2) {
+              const int32_t* __restrict__ head_count, int n_slots, int Nq, int Nk, int Nk_pad, float c2,
+              float* __restrict__ lse, float* __restrict__ o_acc, float* __restrict__ l_acc, int accumulate,
+              int kv_offset_arg) {
+  static_assert(FIXED || !PARTIAL, "key shards use the fixed stabilizer");
   using G = Geo<D, WAVES>;
+  const int kv_offset = PARTIAL ? kv_offset_arg : 0;  // global index of key 0
   constexpr int NS = G::NS, NC = G::NC, BM = G::BM;
   __shared__ __attribute__((aligned(1024))) char lds[2 * G::STAGE_BYTES];  // [stage][K tile, V^T tile]
 
@@ -157,7 +170,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const char* Vth = reinterpret_cast<const char*>(Vt + (size_t)bh * D * Nk_pad);
   const int vt_bytes = (D - 1) * Nk_pad * 2 + kBN * 2;  // one tile's span of V^T rows
 
-  const int kv_end = CAUSAL ? min(Nk, (qt + 1) * BM) : Nk;
+  const int kv_end = CAUSAL ? max(0, min(Nk, (qt + 1) * BM - kv_offset)) : Nk;  // local keys needed
   const int ntiles = (kv_end + kBN - 1) / kBN;
 
   // ---- per-lane, loop-invariant offsets
@@ -182,7 +195,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   auto load_tile = [&](int kt, int stage) {
     load_tiles<D, WAVES>(Kh, Vth, kt, Nk, vt_bytes, lds + stage * G::STAGE_BYTES, wave, gk, gv);
   };
-  load_tile(0, 0);  // first tile in flight before anything else
+  if (ntiles > 0) load_tile(0, 0);  // first tile in flight before anything else
 
   bf16x8 qf[NS];
 #pragma unroll
@@ -199,6 +212,20 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[c][r] = 0.f;
+  if (PARTIAL && accumulate && qvalid) {  // continue the sums of earlier key shards
+    const float* arow = o_acc + qoff;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const float4 t = *reinterpret_cast<const float4*>(arow + c * 32 + 8 * rq + 4 * g);
+        oacc[c][4 * rq + 0] = t.x;
+        oacc[c][4 * rq + 1] = t.y;
+        oacc[c][4 * rq + 2] = t.z;
+        oacc[c][4 * rq + 3] = t.w;
+      }
+    if (g == 0) lsum = l_acc[(size_t)bh * Nq + qrow];
+  }
 
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -214,7 +241,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
   auto visible = [&](int kt, int kb, int r) {
     const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-    return key < Nk && (!CAUSAL || key <= qrow);
+    return key < Nk && (!CAUSAL || kv_offset + key <= qrow);
   };
   // bf16 weights of one block packed for the product; the row sum adds the
   // same rounded weights
@@ -310,8 +337,8 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // tile `it` is in LDS; nobody still reads the other stage
     if (it + 1 < ntiles) load_tile(kt + kBN, ST ^ 1);
-    if (CAUSAL && kt > row0 + 31) return;  // every key of the tile is above this wave's rows
-    const bool need_mask = (kt + kBN > Nk) || (CAUSAL && kt + kBN - 1 > row0);
+    if (CAUSAL && kv_offset + kt > row0 + 31) return;  // every key of the tile is above this wave's rows
+    const bool need_mask = (kt + kBN > Nk) || (CAUSAL && kv_offset + kt + kBN - 1 > row0);
     if constexpr (FIXED) {
       // one straight-line body per mask case
       if (need_mask) tile(it, stage_tag, std::true_type{}, true);
@@ -328,7 +355,21 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // ---- epilogue: the row sum's two halves meet, then O = O_acc / l
   lsum += __shfl_xor(lsum, 32);
+  if constexpr (PARTIAL) {  // key shard: the unnormalized sums
+    if (qvalid) {
+      float* arow = o_acc + qoff;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          *reinterpret_cast<float4*>(arow + c * 32 + 8 * rq + 4 * g) =
+              make_float4(oacc[c][4 * rq], oacc[c][4 * rq + 1], oacc[c][4 * rq + 2], oacc[c][4 * rq + 3]);
+      if (g == 0) l_acc[(size_t)bh * Nq + qrow] = lsum;
+    }
+    return;
+  }
   const float inv = 1.f / lsum;
+  if (qvalid && lse && g == 0) lse[(size_t)bh * Nq + qrow] = kLn2 * ((FIXED ? -negmu : mrow) + log2f(lsum));
   if (qvalid) {
     uint16_t* orow = O + qoff;
 #pragma unroll
@@ -378,21 +419,26 @@ transpose_v(const uint16_t* __restrict__ V, uint16_t* __restrict__ Vt, int Nk, i
   }
 }
 
-template <int D, bool FIXED, bool CAUSAL>
+template <int D, bool FIXED, bool CAUSAL, bool PARTIAL = false>
 hipError_t launch_t(const AttnArgs& a, const uint16_t* vt, int nk_pad, hipStream_t s) {
   constexpr int WAVES = FIXED ? CLIS_FIXED_WAVES : CLIS_ONLINE_WAVES;
   using G = Geo<D, WAVES>;
   const int n_qt = (a.Nq + G::BM - 1) / G::BM;
   const long long blocks = (long long)n_qt * a.n_slots;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  attn_fwd_bf16<D, FIXED, CAUSAL, WAVES><<<(unsigned)blocks, G::THREADS, 0, s>>>(
+  attn_fwd_bf16<D, FIXED, CAUSAL, WAVES, PARTIAL><<<(unsigned)blocks, G::THREADS, 0, s>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), vt, static_cast<uint16_t*>(a.o),
-      a.mu, a.head_list, a.head_count, a.n_slots, a.Nq, a.Nk, nk_pad, a.c2);
+      a.mu, a.head_list, a.head_count, a.n_slots, a.Nq, a.Nk, nk_pad, a.c2, a.lse, a.o_acc, a.l_acc,
+      a.accumulate, a.kv_offset);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, bool fixed, const uint16_t* vt, int nk_pad, hipStream_t s) {
+  if (a.o_acc) {  // key shard
+    if (!fixed) return hipErrorInvalidValue;
+    return a.causal ? launch_t<D, true, true, true>(a, vt, nk_pad, s) : launch_t<D, true, false, true>(a, vt, nk_pad, s);
+  }
   if (fixed) return a.causal ? launch_t<D, true, true>(a, vt, nk_pad, s) : launch_t<D, true, false>(a, vt, nk_pad, s);
   return a.causal ? launch_t<D, false, true>(a, vt, nk_pad, s) : launch_t<D, false, false>(a, vt, nk_pad, s);
 }

@@ -24,7 +24,8 @@ template <int D, bool FIXED, bool CAUSAL>
 __global__ void __launch_bounds__(kRows)
 attn_fwd_fp32(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
               float* __restrict__ O, const float* __restrict__ mu, const int32_t* __restrict__ head_list,
-              const int32_t* __restrict__ head_count, int Nq, int Nk, float c2) {
+              const int32_t* __restrict__ head_count, int Nq, int Nk, float c2, float* __restrict__ lse,
+              float* __restrict__ o_acc, float* __restrict__ l_acc, int accumulate, int kv_offset) {
   __shared__ float Qs[kRows][D + 1];
   __shared__ float Ks[kTile][D];
   __shared__ float Vs[kTile][D];
@@ -53,8 +54,15 @@ attn_fwd_fp32(const float* __restrict__ Q, const float* __restrict__ K, const fl
   for (int c = 0; c < D; ++c) o[c] = 0.f;
   float m = FIXED ? (qvalid ? mu[(size_t)bh * Nq + qrow] : 0.f) : -INFINITY;
   float l = 0.f;
+  if (FIXED && o_acc && accumulate && qvalid) {  // continue the sums of earlier key shards
+    const float* arow = o_acc + ((size_t)bh * Nq + qrow) * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) o[c] = arow[c];
+    l = l_acc[(size_t)bh * Nq + qrow];
+  }
 
-  const int kv_end = CAUSAL ? min(Nk, (qt + 1) * kRows) : Nk;
+  // local keys this block needs (the causal mask compares global indices)
+  const int kv_end = CAUSAL ? max(0, min(Nk, (qt + 1) * kRows - kv_offset)) : Nk;
   for (int kt = 0; kt < kv_end; kt += kTile) {
     __syncthreads();
     for (int i = t; i < kTile * D; i += kRows) {
@@ -70,7 +78,7 @@ attn_fwd_fp32(const float* __restrict__ Q, const float* __restrict__ K, const fl
 #pragma unroll 16
       for (int c = 0; c < D; ++c) s = fmaf(Qs[t][c], Ks[j][c], s);
       const int key = kt + j;
-      const bool ok = key < Nk && (!CAUSAL || key <= qrow);
+      const bool ok = key < Nk && (!CAUSAL || kv_offset + key <= qrow);
       x[j] = ok ? (FIXED ? fmaf(s, c2, -m) : s * c2) : -INFINITY;
     }
     if constexpr (!FIXED) {
@@ -93,8 +101,18 @@ attn_fwd_fp32(const float* __restrict__ Q, const float* __restrict__ K, const fl
       for (int c = 0; c < D; ++c) o[c] = fmaf(p, Vs[j][c], o[c]);
     }
   }
+  if (FIXED && o_acc) {  // key shard: the unnormalized sums
+    if (qvalid) {
+      float* arow = o_acc + ((size_t)bh * Nq + qrow) * D;
+#pragma unroll
+      for (int c = 0; c < D; ++c) arow[c] = o[c];
+      l_acc[(size_t)bh * Nq + qrow] = l;
+    }
+    return;
+  }
   if (qvalid) {
     const float inv = 1.f / l;
+    if (lse) lse[(size_t)bh * Nq + qrow] = 0.693147180559945309f * (m + log2f(l));
     float* orow = O + ((size_t)bh * Nq + qrow) * D;
 #pragma unroll
     for (int c = 0; c < D; ++c) orow[c] = o[c] * inv;
@@ -108,7 +126,8 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   attn_fwd_fp32<D, FIXED, CAUSAL><<<(unsigned)blocks, kRows, 0, s>>>(
       static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
-      static_cast<float*>(a.o), a.mu, a.head_list, a.head_count, a.Nq, a.Nk, a.c2);
+      static_cast<float*>(a.o), a.mu, a.head_list, a.head_count, a.Nq, a.Nk, a.c2, a.lse, a.o_acc, a.l_acc,
+      a.accumulate, a.kv_offset);
   return hipGetLastError();
 }
 

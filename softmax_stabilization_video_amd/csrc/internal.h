@@ -89,6 +89,12 @@ struct AttnArgs {
   int Nq, Nk, d;
   float c2;                   // scale * log2(e), rounded to fp32
   int causal;
+  float* lse = nullptr;       // [BH][Nq] natural-log row log-sum-exp, or NULL
+  // Key-shard form (fixed path): unnormalized fp32 sums instead of O.
+  float* o_acc = nullptr;     // [BH][Nq][d], or NULL for the normal output
+  float* l_acc = nullptr;     // [BH][Nq]
+  int accumulate = 0;         // 1: add to o_acc / l_acc; 0: overwrite them
+  int kv_offset = 0;          // global index of key 0 (causal mask)
 };
 
 // bf16 kernels: V is read through a transposed copy [BH][d][vt_pad(Nk)]
@@ -96,5 +102,9 @@ struct AttnArgs {
 hipError_t launch_transpose_v(const void* v, void* vt, int BH, int Nk, int d, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, bool fixed, const void* vt, hipStream_t s);
 hipError_t launch_attn_fp32(const AttnArgs& a, bool fixed, hipStream_t s);
+
+// O = o_acc / l (bf16 or fp32), and lse = ln 2 (mu + log2 l) if lse is set.
+hipError_t launch_combine(const float* o_acc, const float* l_acc, void* o, int dtype_bf16, const float* mu,
+                          float* lse, long long rows, int d, hipStream_t s);
 
 }  // namespace clis

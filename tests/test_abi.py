@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(clis):
 
 
 def test_abi_version_and_strings(clis):
-    assert clis.lib.clis_abi_version() == 1
+    assert clis.lib.clis_abi_version() == 2
     assert clis.lib.clis_status_string(0) == b"ok"
     assert clis.lib.clis_status_string(5).startswith(b"workspace")
     assert clis.lib.clis_status_string(99) == b"unknown status"
@@ -75,15 +75,16 @@ def _fake(addr=0x10000):
     (dict(q=0x10008), 4),                # not 16-byte aligned
     (dict(ws=None, mode=0), 5),          # auto mode needs a workspace
     (dict(ws_bytes=10, mode=0), 5),
+    (dict(lse=0x60002), 4),              # lse_out not 4-byte aligned
 ])
 def test_argument_checks_reject_before_launch(clis, case, expected):
     a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, B=1, H=2, Nq=10, Nk=10, d=64, scale=0.125,
-             causal=0, dtype=0, mode=1, ws=0x50000, ws_bytes=1 << 30)
+             causal=0, dtype=0, mode=1, ws=0x50000, ws_bytes=1 << 30, lse=None)
     a.update(case)
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
     st = clis.lib.clis_attn_fwd(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), a["B"], a["H"], a["Nq"],
                                 a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], a["mode"], None, None,
-                                None, vp(a["ws"]), a["ws_bytes"], None)
+                                None, vp(a["lse"]), vp(a["ws"]), a["ws_bytes"], None)
     assert st == expected, clis.lib.clis_last_error()
     assert clis.lib.clis_last_error() != b""
 
@@ -92,11 +93,52 @@ def test_empty_batch_is_a_no_op(clis):
     # nothing to compute: CLIS_OK without touching any pointer
     for B, H, Nq in ((0, 4, 10), (2, 0, 10), (2, 4, 0)):
         assert clis.lib.clis_attn_fwd(None, None, None, None, B, H, Nq, 10, 128, 0.1, 0, 0, 0, None, None,
-                                      None, None, 0, None) == 0
-        assert clis.lib.online_attn_fwd(None, None, None, None, B, H, Nq, 10, 128, 0.1, 0, 0, None, 0,
+                                      None, None, None, 0, None) == 0
+        assert clis.lib.online_attn_fwd(None, None, None, None, B, H, Nq, 10, 128, 0.1, 0, 0, None, None, 0,
                                         None) == 0
+        assert clis.lib.clis_attn_fwd_partial(None, None, None, B, H, Nq, 10, 128, 0.1, 0, 0, None, 0, 0, None,
+                                              None, None, 0, None) == 0
+        assert clis.lib.clis_attn_combine(None, None, None, B, H, Nq, 128, 0, None, None, None) == 0
         assert clis.lib.clis_certify(None, None, None, B, H, Nq, 10, 128, 0.1, 0, None, None, None, None,
                                      None, 0, None) == 0
+
+
+@pytest.mark.parametrize("case,expected", [
+    (dict(mu=None), 1),
+    (dict(o_acc=None), 1),
+    (dict(o_acc=0x60008), 4),            # fp32 accumulators need 16-byte alignment
+    (dict(kv_offset=-1), 2),
+    (dict(accumulate=2), 2),
+    (dict(d=80), 3),
+    (dict(ws=None), 5),                  # bf16 shards need a workspace for V^T
+    (dict(Nk=0), 2),
+])
+def test_partial_argument_checks(clis, case, expected):
+    a = dict(q=0x10000, k=0x20000, v=0x30000, B=1, H=2, Nq=10, Nk=6, d=64, mu=0x40000, kv_offset=4,
+             accumulate=1, o_acc=0x60000, l_acc=0x70000, ws=0x50000)
+    a.update(case)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = clis.lib.clis_attn_fwd_partial(vp(a["q"]), vp(a["k"]), vp(a["v"]), a["B"], a["H"], a["Nq"], a["Nk"],
+                                        a["d"], 0.125, 1, 0, vp(a["mu"]), a["kv_offset"], a["accumulate"],
+                                        vp(a["o_acc"]), vp(a["l_acc"]), vp(a["ws"]), 1 << 30, None)
+    assert st == expected, clis.lib.clis_last_error()
+
+
+@pytest.mark.parametrize("case,expected", [
+    (dict(o=None), 1),
+    (dict(lse=0x40000, mu=None), 1),     # the log-sum-exp needs the stabilizers
+    (dict(d=96), 3),
+    (dict(dtype=5), 3),
+    (dict(o=0x30004), 4),
+    (dict(B=-2), 2),
+])
+def test_combine_argument_checks(clis, case, expected):
+    a = dict(o_acc=0x10000, l_acc=0x20000, o=0x30000, B=1, H=2, Nq=10, d=128, dtype=0, mu=None, lse=None)
+    a.update(case)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = clis.lib.clis_attn_combine(vp(a["o_acc"]), vp(a["l_acc"]), vp(a["o"]), a["B"], a["H"], a["Nq"], a["d"],
+                                    a["dtype"], vp(a["mu"]), vp(a["lse"]), None)
+    assert st == expected, clis.lib.clis_last_error()
 
 
 def test_certify_requires_outputs(clis):
