@@ -185,6 +185,60 @@ def parity(w, Q, K, V, o_step, cert, sample):
             "flags_equal": f"{agree}/{w.B * w.H}", "vs": "fp64 oracle"}
 
 
+# Fallback-rate and dispatch-cost sweep: synthetic inputs on the wan720p
+# shape (B1 H20 d128) with one parameter varied at a time.  "heads" scaled by
+# fail_qk_scale (and with outlier_frac of their key rows scaled by
+# outlier_scale) are pushed toward or past the certificate's cap.
+SWEEP = [
+    ("failing_head_fraction", "fail_frac", (0.0, 0.1, 0.25, 0.5, 0.75, 1.0),
+     dict(fail_qk_scale=40.0, outlier_frac=0.0, outlier_scale=1.0), 75600),
+    ("qk_scale_all_heads", "fail_qk_scale", (1.0, 1.5, 1.9, 2.0, 2.02, 2.04, 2.1, 3.0),
+     dict(fail_frac=1.0, outlier_frac=0.0, outlier_scale=1.0), 75600),
+    ("outlier_key_scale_all_heads", "outlier_scale", (1.0, 2.0, 2.5, 2.8, 3.0, 3.5, 8.0),
+     dict(fail_frac=1.0, fail_qk_scale=1.0, outlier_frac=0.001), 75600),
+    ("tokens_at_qk_scale_2.04", "N", (17160, 32760, 65536, 75600),
+     dict(fail_frac=1.0, fail_qk_scale=2.04, outlier_frac=0.0, outlier_scale=1.0), None),
+]
+
+
+def sweep(reps: int):
+    """Certification rate and auto-mode throughput (certify inside) against
+    the online kernel, for every point of SWEEP."""
+    import torch
+    import workloads
+    import softmax_stabilization_video_amd as clis
+    points = []
+    for name, param, values, fixed, N in SWEEP:
+        for val in values:
+            kw = dict(fixed)
+            n = int(val) if param == "N" else N
+            if param != "N":
+                kw[param] = val
+            w = workloads.custom(f"sweep_{name}", 1, 20, n, 128, "bf16", False, key_bias_std=2.0, **kw)
+            Q, K, V = workloads.make_inputs(w, 0)
+            q, k, v = (workloads.to_torch(a, w.dtype) for a in (Q, K, V))
+            o = torch.empty_like(q)
+            ws = clis.new_workspace(w.B, w.H, w.Nq, w.Nk, w.d)
+            stream = torch.cuda.current_stream()
+            auto = lambda: clis.clis_attn_fwd(q, k, v, w.scale, mode="auto", out=o, workspace=ws)
+            onl = lambda: clis.online_attn_fwd(q, k, v, w.scale, out=o, workspace=ws)
+            for f in (auto, onl):
+                f()
+            _, cert = clis.clis_certify(q, k, v, w.scale, workspace=ws)
+            t_auto = statistics.median(time_calls(auto, reps, stream))
+            t_onl = statistics.median(time_calls(onl, reps, stream))
+            n_cert = int(cert.sum().item())
+            fl = w.flops()
+            points.append({"sweep": name, param: val, "N": n, "certified": n_cert, "heads": w.B * w.H,
+                           "auto_ms": round(t_auto, 3), "online_ms": round(t_onl, 3),
+                           "auto_tflops": round(fl / t_auto / 1e9, 1), "online_tflops": round(fl / t_onl / 1e9, 1),
+                           "speedup_vs_online": round(t_onl / t_auto, 4)})
+            log(json.dumps(points[-1]))
+            del q, k, v, o, ws, Q, K, V
+            torch.cuda.empty_cache()
+    return points
+
+
 def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -199,6 +253,9 @@ def main(argv=None):
     p.add_argument("--reps", type=int, default=20, help="calls per extra timing")
     p.add_argument("--calibrate-copy-mb", type=float, default=0.0,
                    help="also run one plain device copy of this many MiB (scales HBM counters)")
+    p.add_argument("--sweep", action="store_true",
+                   help="instead of the step benchmark: certification rate and auto-mode throughput vs input "
+                        "scale, outlier keys, failing-head fraction and tokens (one JSON line)")
     args = p.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -214,6 +271,10 @@ def main(argv=None):
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+    if args.sweep:
+        print(json.dumps({"sweep": sweep(max(3, min(args.reps, 7))), "unit": "ms / TFLOP/s",
+                          "data": "synthetic (seeded Gaussians, wan720p shape B1 H20 d128 bf16)"}), flush=True)
+        return
     w = workloads.WORKLOADS[args.workload]
     log(f"workload {w.name}: B={w.B} H={w.H} Nq={w.Nq} Nk={w.Nk} d={w.d} {w.dtype} causal={w.causal}")
     t0 = time.perf_counter()
