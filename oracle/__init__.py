@@ -70,7 +70,7 @@ def _load(path):
     L.oracle_attention_rows.argtypes = [dp, dp, dp, i64, i64, ci, cd, ci, ip, i64, dp]
     L.oracle_certify_head.argtypes = [dp, dp, dp, i64, i64, ci, cd, ci, dp, dp, ctypes.POINTER(CertRecord)]
     L.oracle_fixed_mu_rows.argtypes = [dp, dp, dp, i64, i64, ci, cd, ci, dp, ip, i64, dp, dp, dp]
-    L.oracle_online_rows.argtypes = [dp, dp, dp, i64, i64, ci, cd, ci, i64, ip, i64, dp]
+    L.oracle_online_rows.argtypes = [dp, dp, dp, i64, i64, ci, cd, ci, i64, cd, ip, i64, dp]
     L.oracle_lse_rows.argtypes = [dp, dp, i64, i64, ci, cd, ci, ip, i64, dp]
     L.oracle_fixed_mu_partial_rows.argtypes = [dp, dp, dp, i64, i64, ci, cd, ci, dp, i64, i64, ip, i64, dp, dp]
     for f in (L.oracle_attention_rows, L.oracle_certify_head, L.oracle_fixed_mu_rows,
@@ -214,8 +214,10 @@ def fixed_mu_head(q, k, v, scale: float, mu, causal: bool = False, rows=None, th
 
 
 def online_head(q, k, v, scale: float, causal: bool = False, block: int = 64, rows=None,
-                threads: int | None = None):
-    """Output evaluated with online softmax over key blocks of `block` keys."""
+                threads: int | None = None, tau: float = 0.0):
+    """Output evaluated with online softmax over key blocks of `block` keys;
+    tau > 0: rescale only when a block maximum exceeds the stabilizer in use
+    by more than tau (log2 units)."""
     q, k, v = (np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v))
     nq, d = q.shape
     nk = k.shape[0]
@@ -225,7 +227,7 @@ def online_head(q, k, v, scale: float, causal: bool = False, block: int = 64, ro
 
     def run(a, b):
         L.oracle_online_rows(_p(q), _p(k), _p(v), nq, nk, d, float(scale), int(causal), int(block),
-                             _p(rows[a:b], ctypes.c_int64), b - a, _p(out[a:b]))
+                             float(tau), _p(rows[a:b], ctypes.c_int64), b - a, _p(out[a:b]))
 
     _fanout(run, rows, threads or default_threads())
     return out

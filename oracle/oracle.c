@@ -268,11 +268,15 @@ int oracle_fixed_mu_rows(const double* q, const double* k, const double* v,
  * Self-check: online softmax over key blocks of `block` keys [CLiS abstract:
  * the baseline keeps a running maximum and rescales its accumulators].
  * Per block: m' = max(m, block max), alpha = 2^{m - m'}, l = alpha l + sum p,
- * o = alpha o + sum p v, with p = 2^{c s - m'}.  Must equal the definition.
+ * o = alpha o + sum p v, with p = 2^{c s - m'}.  With tau > 0 the rescale is
+ * lazy (the conditional rescaling of FlashAttention-4, which the pages name as
+ * a comparator): the stabilizer in use changes only when a block's maximum
+ * exceeds it by more than tau, so every weight stays at most 2^tau.  tau = 0 is
+ * the eager form.  Both must equal the definition.
  */
 int oracle_online_rows(const double* q, const double* k, const double* v,
                        int64_t nq, int64_t nk, int d, double scale, int causal, int64_t block,
-                       const int64_t* rows, int64_t nrows, double* out) {
+                       double tau, const int64_t* rows, int64_t nrows, double* out) {
   (void)nq;
   const double c2 = scale * LOG2E;
   double* s = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
@@ -289,7 +293,7 @@ int oracle_online_rows(const double* q, const double* k, const double* v,
       const int64_t j1 = (j0 + block < n) ? j0 + block : n;
       double mb = -INFINITY;
       for (int64_t j = j0; j < j1; ++j) mb = (c2 * s[j] > mb) ? c2 * s[j] : mb;
-      const double mn = mb > m ? mb : m;
+      const double mn = (mb > m + tau) ? mb : m;
       const double alpha = exp2(m - mn);
       l *= alpha;
       for (int c = 0; c < d; ++c) o[c] *= alpha;

@@ -131,7 +131,8 @@ def pin_weights_sum_to_one():
 
 
 def pin_other_evaluations_agree():
-    """The fixed-stabilizer and online evaluations give the definition's output."""
+    """The fixed-stabilizer and online (eager and lazy-rescale) evaluations
+    give the definition's output."""
     rng = _rng(5)
     nq, nk, d = 17, 40, 8
     q = rng.standard_normal((nq, d))
@@ -145,7 +146,17 @@ def pin_other_evaluations_agree():
         of, _, _ = oracle.fixed_mu_head(q, kk, vv, scale, rec["mu"], causal)
         np.testing.assert_allclose(of, o, atol=1e-12)
         for block in (1, 3, 16, 64):
-            np.testing.assert_allclose(oracle.online_head(q, kk, vv, scale, causal, block), o, atol=1e-12)
+            for tau in (0.0, 1.0, 8.0):  # eager, and lazy rescaling at two thresholds
+                np.testing.assert_allclose(oracle.online_head(q, kk, vv, scale, causal, block, tau=tau), o,
+                                           atol=1e-12)
+    # scores growing by ~72 log2 units per key: a stabilizer that stops moving
+    # overflows fp64 within a few blocks
+    qs, ks = np.ones((3, 1)), (50.0 * np.arange(40.0))[:, None]
+    vs = rng.standard_normal((40, 2))
+    want = oracle.attention_head(qs, ks, vs, 1.0)
+    for tau in (0.0, 8.0):
+        for block in (1, 4):
+            np.testing.assert_allclose(oracle.online_head(qs, ks, vs, 1.0, False, block, tau=tau), want, atol=1e-12)
 
 
 # ------------------------------------------------------------ certification

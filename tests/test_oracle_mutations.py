@@ -39,6 +39,8 @@ MUTANTS = {
     "mu_sign": ("mu[r] = c2 * dot;", "mu[r] = -c2 * dot;"),
     "online_forgets_rescale": ("      l *= alpha;\n", "      l *= 1.0;\n"),
     "online_rescale_wrong_way": ("const double alpha = exp2(m - mn);", "const double alpha = exp2(mn - m);"),
+    "lazy_stabilizer_never_moves": ("const double mn = (mb > m + tau) ? mb : m;",
+                                    "const double mn = (m == -INFINITY) ? mb : m;"),
     "lse_log2_not_ln": ("lse[t] = m + log(sum);", "lse[t] = m + log2(sum);"),
     "lse_drops_shift": ("for (int64_t j = 0; j < n; ++j) sum += exp(s[j] - m);",
                         "for (int64_t j = 0; j < n; ++j) sum += exp(s[j]);"),
