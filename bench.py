@@ -9,7 +9,8 @@ certifies internally.  The workload defaults to the Wan 2.2 720p x 81-frame
 shape at one GPU's share of heads (B=1, H=20, N=75,600, d=128, bf16).
 
 Printed: ONE JSON line with the step throughput (attention TFLOP/s), the
-CLiS kernel alone, the online-softmax baseline, their speedup, the roofline
+CLiS kernel alone, the online-softmax baseline and its lazy-rescale form
+(FlashAttention-4's conditional rescaling), the speedups, the roofline
 of the dominant kernel (the fixed-stabilizer attention kernel; per-launch
 durations from HIP events on the stream the library launches on), the rate
 of an MFMA-only probe on the same GPU, the fp64 CPU oracle timed on a
@@ -41,8 +42,8 @@ def dominant_kernel(w):
     """(name, source) of the fixed-stabilizer kernel that runs this workload."""
     c = "true" if w.causal else "false"
     if w.dtype == "bf16":
-        return f"attn_fwd_bf16<{w.d}, true, {c}, 8, false>", os.path.join(CSRC, "attn_bf16.hip")
-    return f"attn_fwd_fp32<{w.d}, true, {c}>", os.path.join(CSRC, "attn_fp32.hip")
+        return f"attn_fwd_bf16<{w.d}, true, {c}, 8, false, false>", os.path.join(CSRC, "attn_bf16.hip")
+    return f"attn_fwd_fp32<{w.d}, true, {c}, false>", os.path.join(CSRC, "attn_fp32.hip")
 
 
 def log(*a):
@@ -317,8 +318,12 @@ def main(argv=None):
         res["fixed_kernel_ms_mean"] = statistics.mean(fixed)
         res["fixed_kernel_ms_median"] = statistics.median(fixed)
     if args.only in ("all", "online"):
-        onl = time_calls(lambda: clis.online_attn_fwd(q, k, v, w.scale, w.causal, out=o), args.reps, stream)
+        onl = time_calls(lambda: clis.online_attn_fwd(q, k, v, w.scale, w.causal, out=o, workspace=ws),
+                         args.reps, stream)
         res["online_ms"] = statistics.median(onl)
+        lazy = time_calls(lambda: clis.clis_attn_fwd(q, k, v, w.scale, w.causal, mode="online_lazy", out=o,
+                                                     workspace=ws), args.reps, stream)
+        res["online_lazy_ms"] = statistics.median(lazy)
     if args.only in ("all", "certify"):
         cer = time_calls(lambda: clis.clis_certify(q, k, v, w.scale, workspace=ws), args.reps, stream)
         res["certify_ms"] = statistics.median(cer)
@@ -354,6 +359,11 @@ def main(argv=None):
         out["speedup_vs_online"] = round(res["online_ms"] / ms_step, 4)
         if "clis_kernel_ms" in res:
             out["kernel_speedup_vs_online"] = round(res["online_ms"] / res["clis_kernel_ms"], 4)
+    if "online_lazy_ms" in res:
+        out["online_lazy_tflops"] = round(flops / res["online_lazy_ms"] / 1e9, 2)
+        out["online_lazy_ms"] = round(res["online_lazy_ms"], 4)
+        if "clis_kernel_ms" in res:
+            out["kernel_speedup_vs_online_lazy"] = round(res["online_lazy_ms"] / res["clis_kernel_ms"], 4)
     if "certify_ms" in res:
         out["certify_ms"] = round(res["certify_ms"], 4)
     if "fixed_kernel_ms_mean" in res:

@@ -57,7 +57,11 @@ typedef enum {
   CLIS_MODE_AUTO = 0,   /* certified heads: fixed stabilizer; the rest: online softmax */
   CLIS_MODE_FIXED = 1,  /* every head on the fixed-stabilizer kernel (testing tool: an
                            uncertified head may overflow to Inf/NaN) */
-  CLIS_MODE_ONLINE = 2  /* every head on the online-softmax kernel */
+  CLIS_MODE_ONLINE = 2,  /* every head on the online-softmax kernel */
+  CLIS_MODE_ONLINE_LAZY = 3  /* every head on online softmax with conditional rescaling: the
+                                stabilizer in use moves, and the accumulators are rescaled, only
+                                when a row's tile maximum exceeds it by more than 8 (log2 units),
+                                as FlashAttention-4 does (a comparator the CLiS pages name) */
 } clis_mode_t;
 
 typedef enum {

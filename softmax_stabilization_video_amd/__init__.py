@@ -30,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libclis.so")
 
 CLIS_BF16, CLIS_FP32 = 0, 1
-MODES = {"auto": 0, "fixed": 1, "online": 2}
+MODES = {"auto": 0, "fixed": 1, "online": 2, "online_lazy": 3}
 STATUS = {0: "CLIS_OK", 1: "CLIS_ERR_NULL", 2: "CLIS_ERR_SHAPE", 3: "CLIS_ERR_UNSUPPORTED",
           4: "CLIS_ERR_ALIGN", 5: "CLIS_ERR_WORKSPACE", 6: "CLIS_ERR_HIP"}
 EXPORTS = ["clis_workspace_bytes", "clis_certify", "clis_attn_fwd", "online_attn_fwd",

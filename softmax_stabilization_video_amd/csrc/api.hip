@@ -138,8 +138,10 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
                   const int32_t* cert, int32_t* route_out, float* lse_out, void* ws, size_t ws_bytes,
                   void* stream) {
   g_err[0] = 0;
-  if (mode != CLIS_MODE_AUTO && mode != CLIS_MODE_FIXED && mode != CLIS_MODE_ONLINE)
+  if (mode != CLIS_MODE_AUTO && mode != CLIS_MODE_FIXED && mode != CLIS_MODE_ONLINE &&
+      mode != CLIS_MODE_ONLINE_LAZY)
     return fail(CLIS_ERR_UNSUPPORTED, "unknown mode %d", mode);
+  const bool all_online = (mode == CLIS_MODE_ONLINE || mode == CLIS_MODE_ONLINE_LAZY);
   bool empty = false;
   int st = check_common(B, H, Nq, Nk, d, scale, dtype, causal, &empty);
   if (st != CLIS_OK || empty) return st;
@@ -148,7 +150,8 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   clis::AttnArgs a = attn_args(q, k, v, o, B, H, Nq, Nk, d, scale, causal);
   a.lse = lse_out;
-  const bool plain_online = (mode == CLIS_MODE_ONLINE && !route_out);
+  a.lazy = (mode == CLIS_MODE_ONLINE_LAZY);
+  const bool plain_online = (all_online && !route_out);
   if (!plain_online || needs_vt(dtype)) {
     if ((st = check_ws(ws, ws_bytes, B, H, Nq, Nk, d)) != CLIS_OK) return st;
   }
@@ -183,7 +186,7 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
 
   // Each kernel's grid covers every head; slots past its list's count exit
   // at once, so the routing needs no host round trip.
-  if (mode != CLIS_MODE_ONLINE) {
+  if (!all_online) {
     clis::AttnArgs f = a;
     f.mu = mu_use;
     f.head_list = lists;

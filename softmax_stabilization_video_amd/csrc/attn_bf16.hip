@@ -7,7 +7,12 @@
 //             Stabilization", abstract and Figure 5(a));
 //   ONLINE -- online softmax: per key tile a running row maximum and a
 //             rescale factor alpha for the row sum and the output accumulator
-//             (the baseline those pages compare against).
+//             (the baseline those pages compare against);
+//   ONLINE, LAZY -- online softmax with conditional rescaling (the form of
+//             FlashAttention-4, which those pages name as a comparator): the
+//             stabilizer in use moves, and the accumulators are rescaled, only
+//             when a row's tile maximum exceeds it by more than kLazyTau (log2
+//             units), under a wave-uniform branch; weights stay <= 2^kLazyTau.
 // The two variants use independently tuned workgroup sizes (the pages tune
 // tiles per method too, Table 7 caption).
 //
@@ -76,6 +81,7 @@ constexpr int kBN = 64;                   // keys per tile
 constexpr int kXcds = 8;                  // MI355X: workgroups are dealt round-robin to 8 XCDs
 constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor word 3 (untyped 32-bit data)
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLazyTau = 8.f;  // log2 units: lazy-rescale weights stay <= 256
 
 __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -136,7 +142,7 @@ __device__ __forceinline__ void load_tiles(const char* Kh, const char* Vth, int 
   }
 }
 
-template <int D, bool FIXED, bool CAUSAL, int WAVES, bool PARTIAL>
+template <int D, bool FIXED, bool CAUSAL, int WAVES, bool PARTIAL, bool LAZY>
 __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2)
 attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ Vt, uint16_t* __restrict__ O,
@@ -145,6 +151,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               float* __restrict__ lse, float* __restrict__ o_acc, float* __restrict__ l_acc, int accumulate,
               int kv_offset_arg) {
   static_assert(FIXED || !PARTIAL, "key shards use the fixed stabilizer");
+  static_assert(!(FIXED && LAZY), "lazy rescaling is an online-softmax form");
   using G = Geo<D, WAVES>;
   const int kv_offset = PARTIAL ? kv_offset_arg : 0;  // global index of key 0
   constexpr int NS = G::NS, NC = G::NC, BM = G::BM;
@@ -294,34 +301,50 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const floatx16 s0 = qk(Ks, 0);
       const floatx16 s1 = qk(Ks, 1);
       // online softmax: the tile maximum must be known before any weight,
-      // and every weight waits for it
+      // and every weight waits for it (c > 0, so the maximum of c s is c
+      // times the maximum of s)
       float x[2][16];
       float tmax = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        x[0][r] = s0[r] * c2;
-        x[1][r] = s1[r] * c2;
+        x[0][r] = s0[r];
+        x[1][r] = s1[r];
         if (need_mask) {
           x[0][r] = visible(kt, 0, r) ? x[0][r] : -INFINITY;
           x[1][r] = visible(kt, 1, r) ? x[1][r] : -INFINITY;
         }
         tmax = fmaxf(tmax, fmaxf(x[0][r], x[1][r]));
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(mrow, tmax);
-      const bool none = (mnew == -INFINITY);  // no visible key yet
-      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(mrow - mnew);
-      const float msub = none ? 0.f : mnew;
-      mrow = mnew;
-      lsum *= alpha;
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c2;
+      float msub;
+      auto rescale = [&](float alpha) {
+        lsum *= alpha;
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
+        for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[c][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[c][r] *= alpha;
+      };
+      if constexpr (LAZY) {
+        // a row moves its stabilizer only past a growth of kLazyTau; the
+        // rescale runs when any row of the wave moved (-inf: no key seen yet)
+        const bool grow = tmax > mrow + kLazyTau;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float mnew = grow ? tmax : mrow;
+          rescale(grow ? __builtin_amdgcn_exp2f(mrow - mnew) : 1.f);
+          mrow = mnew;
+        }
+        msub = (mrow == -INFINITY) ? 0.f : mrow;
+      } else {
+        const float mnew = fmaxf(mrow, tmax);
+        const bool none = (mnew == -INFINITY);  // no visible key yet
+        rescale(none ? 1.f : __builtin_amdgcn_exp2f(mrow - mnew));
+        msub = none ? 0.f : mnew;
+        mrow = mnew;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        x[0][r] = __builtin_amdgcn_exp2f(x[0][r] - msub);
-        x[1][r] = __builtin_amdgcn_exp2f(x[1][r] - msub);
+        x[0][r] = __builtin_amdgcn_exp2f(fmaf(x[0][r], c2, -msub));
+        x[1][r] = __builtin_amdgcn_exp2f(fmaf(x[1][r], c2, -msub));
       }
       uint32_t pw0[8], pw1[8];
       pack(x[0], pw0);
@@ -419,14 +442,14 @@ transpose_v(const uint16_t* __restrict__ V, uint16_t* __restrict__ Vt, int Nk, i
   }
 }
 
-template <int D, bool FIXED, bool CAUSAL, bool PARTIAL = false>
+template <int D, bool FIXED, bool CAUSAL, bool PARTIAL = false, bool LAZY = false>
 hipError_t launch_t(const AttnArgs& a, const uint16_t* vt, int nk_pad, hipStream_t s) {
   constexpr int WAVES = FIXED ? CLIS_FIXED_WAVES : CLIS_ONLINE_WAVES;
   using G = Geo<D, WAVES>;
   const int n_qt = (a.Nq + G::BM - 1) / G::BM;
   const long long blocks = (long long)n_qt * a.n_slots;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  attn_fwd_bf16<D, FIXED, CAUSAL, WAVES, PARTIAL><<<(unsigned)blocks, G::THREADS, 0, s>>>(
+  attn_fwd_bf16<D, FIXED, CAUSAL, WAVES, PARTIAL, LAZY><<<(unsigned)blocks, G::THREADS, 0, s>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), vt, static_cast<uint16_t*>(a.o),
       a.mu, a.head_list, a.head_count, a.n_slots, a.Nq, a.Nk, nk_pad, a.c2, a.lse, a.o_acc, a.l_acc,
       a.accumulate, a.kv_offset);
@@ -440,6 +463,9 @@ hipError_t launch_d(const AttnArgs& a, bool fixed, const uint16_t* vt, int nk_pa
     return a.causal ? launch_t<D, true, true, true>(a, vt, nk_pad, s) : launch_t<D, true, false, true>(a, vt, nk_pad, s);
   }
   if (fixed) return a.causal ? launch_t<D, true, true>(a, vt, nk_pad, s) : launch_t<D, true, false>(a, vt, nk_pad, s);
+  if (a.lazy)
+    return a.causal ? launch_t<D, false, true, false, true>(a, vt, nk_pad, s)
+                    : launch_t<D, false, false, false, true>(a, vt, nk_pad, s);
   return a.causal ? launch_t<D, false, true>(a, vt, nk_pad, s) : launch_t<D, false, false>(a, vt, nk_pad, s);
 }
 

@@ -20,7 +20,7 @@ namespace {
 constexpr int kRows = 64;
 constexpr int kTile = 32;
 
-template <int D, bool FIXED, bool CAUSAL>
+template <int D, bool FIXED, bool CAUSAL, bool LAZY>
 __global__ void __launch_bounds__(kRows)
 attn_fwd_fp32(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
               float* __restrict__ O, const float* __restrict__ mu, const int32_t* __restrict__ head_list,
@@ -81,7 +81,21 @@ attn_fwd_fp32(const float* __restrict__ Q, const float* __restrict__ K, const fl
       const bool ok = key < Nk && (!CAUSAL || kv_offset + key <= qrow);
       x[j] = ok ? (FIXED ? fmaf(s, c2, -m) : s * c2) : -INFINITY;
     }
-    if constexpr (!FIXED) {
+    if constexpr (LAZY) {
+      // conditional rescaling: the stabilizer moves only when the tile
+      // maximum exceeds it by more than 8 (log2 units); weights stay <= 256
+      float tmax = -INFINITY;
+      for (int j = 0; j < kTile; ++j) tmax = fmaxf(tmax, x[j]);
+      if (tmax > m + 8.f) {
+        const float alpha = __builtin_amdgcn_exp2f(m - tmax);  // 0 while m = -inf
+        l *= alpha;
+#pragma unroll
+        for (int c = 0; c < D; ++c) o[c] *= alpha;
+        m = tmax;
+      }
+      const float msub = (m == -INFINITY) ? 0.f : m;
+      for (int j = 0; j < kTile; ++j) x[j] -= msub;
+    } else if constexpr (!FIXED) {
       float tmax = -INFINITY;
       for (int j = 0; j < kTile; ++j) tmax = fmaxf(tmax, x[j]);
       const float mnew = fmaxf(m, tmax);
@@ -119,12 +133,12 @@ attn_fwd_fp32(const float* __restrict__ Q, const float* __restrict__ K, const fl
   }
 }
 
-template <int D, bool FIXED, bool CAUSAL>
+template <int D, bool FIXED, bool CAUSAL, bool LAZY = false>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   const int n_qt = (a.Nq + kRows - 1) / kRows;
   const long long blocks = (long long)n_qt * a.n_slots;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  attn_fwd_fp32<D, FIXED, CAUSAL><<<(unsigned)blocks, kRows, 0, s>>>(
+  attn_fwd_fp32<D, FIXED, CAUSAL, LAZY><<<(unsigned)blocks, kRows, 0, s>>>(
       static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
       static_cast<float*>(a.o), a.mu, a.head_list, a.head_count, a.Nq, a.Nk, a.c2, a.lse, a.o_acc, a.l_acc,
       a.accumulate, a.kv_offset);
@@ -134,6 +148,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
 template <int D>
 hipError_t launch_d(const AttnArgs& a, bool fixed, hipStream_t s) {
   if (fixed) return a.causal ? launch_t<D, true, true>(a, s) : launch_t<D, true, false>(a, s);
+  if (a.lazy) return a.causal ? launch_t<D, false, true, true>(a, s) : launch_t<D, false, false, true>(a, s);
   return a.causal ? launch_t<D, false, true>(a, s) : launch_t<D, false, false>(a, s);
 }
 

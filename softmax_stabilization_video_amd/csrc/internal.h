@@ -95,6 +95,7 @@ struct AttnArgs {
   float* l_acc = nullptr;     // [BH][Nq]
   int accumulate = 0;         // 1: add to o_acc / l_acc; 0: overwrite them
   int kv_offset = 0;          // global index of key 0 (causal mask)
+  int lazy = 0;               // online path: conditional (lazy) rescaling
 };
 
 // bf16 kernels: V is read through a transposed copy [BH][d][vt_pad(Nk)]

@@ -67,7 +67,7 @@ def test_lse_every_mode(clis, case):
     want = _oracle_lse(w, host)
     mu, cert = clis.clis_certify(*dev, w.scale)
     outs = {}
-    for m in ("fixed", "online", "auto"):
+    for m in ("fixed", "online", "online_lazy", "auto"):
         say("lse", m, name)
         o, lse = clis.clis_attn_fwd(*dev, w.scale, causal, mode=m, mu=mu, cert=cert, want_lse=True)
         plain = clis.clis_attn_fwd(*dev, w.scale, causal, mode=m, mu=mu, cert=cert)

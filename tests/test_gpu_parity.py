@@ -7,7 +7,8 @@ decision B_h <= C taken in fp64 on both sides; each case first asserts that
 the oracle's B_h is not within 1e-9 (relative) of C, where the two fp64
 summation orders could disagree.
 Attention: bf16 within max abs 2e-2, mean abs 1e-3 and rel L2 5e-3 of the
-oracle; fp32 within max abs 1e-5.  Routing: auto mode's output for every
+oracle; fp32 within max abs 1e-5; in every mode (fixed, online, online with
+lazy rescaling, auto).  Routing: auto mode's output for every
 head is bitwise equal to the forced mode of the route it took.
 """
 import math
@@ -60,7 +61,7 @@ def check_certify(clis, w, host, dev, margin=1e-9):
     return mu, cert, ref
 
 
-def run_attention(clis, w, host, dev, mu, cert, rows=None, modes=("fixed", "online", "auto")):
+def run_attention(clis, w, host, dev, mu, cert, rows=None, modes=("fixed", "online", "online_lazy", "auto")):
     """Every mode on the device, compared with the oracle (all rows or `rows`)."""
     import torch
     want = oracle.attention(*host, w.dtype, w.scale, w.causal, rows=rows)
@@ -73,7 +74,7 @@ def run_attention(clis, w, host, dev, mu, cert, rows=None, modes=("fixed", "onli
         r = route.cpu().numpy()
         if m == "fixed":
             assert np.all(r == 1)
-        elif m == "online":
+        elif m in ("online", "online_lazy"):
             assert np.all(r == 0)
         else:
             assert np.array_equal(r, cert.cpu().numpy())
