@@ -142,7 +142,7 @@ __device__ __forceinline__ void load_tiles(const char* Kh, const char* Vth, int 
   }
 }
 
-template <int D, bool FIXED, bool CAUSAL, int WAVES, bool PARTIAL, bool LAZY>
+template <int D, bool FIXED, bool CAUSAL, int WAVES, bool PARTIAL, bool LAZY, bool PRESCALE>
 __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2)
 attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ Vt, uint16_t* __restrict__ O,
@@ -152,6 +152,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               int kv_offset_arg) {
   static_assert(FIXED || !PARTIAL, "key shards use the fixed stabilizer");
   static_assert(!(FIXED && LAZY), "lazy rescaling is an online-softmax form");
+  static_assert(!PRESCALE || (FIXED && !PARTIAL), "pre-scaled queries: fixed path, output O only");
   using G = Geo<D, WAVES>;
   const int kv_offset = PARTIAL ? kv_offset_arg : 0;  // global index of key 0
   constexpr int NS = G::NS, NC = G::NC, BM = G::BM;
@@ -213,6 +214,18 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
   float mrow = FIXED ? (qvalid ? mu[(size_t)bh * Nq + qrow] : 0.f) : -INFINITY;
   const float negmu = -mrow;
+  // PRESCALE: the query fragments hold q' = bf16(c q) and every score product
+  // starts from -mu, so each accumulator ends as the exp2 argument
+  // x = c q.k - mu itself and a weight costs one v_exp_f32 (no fma per score).
+  floatx16 nmu;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) nmu[r] = negmu;
+  if constexpr (PRESCALE) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)((float)qf[s][e] * c2);  // round to nearest even
+  }
   float lsum = 0.f;
   floatx16 oacc[NC];
 #pragma unroll
@@ -241,6 +254,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     floatx16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    if constexpr (PRESCALE) acc = nmu;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       acc = mfma32(*reinterpret_cast<const bf16x8*>(Ks + kb * 32 * D * 2 + kro[s]), qf[s], acc);
@@ -277,13 +291,14 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const char* Ks = lds + ST * G::STAGE_BYTES;
     const char* Vs = Ks + G::TILE_BYTES;
     if constexpr (FIXED) {
-      // no running maximum: x = c s - mu with mu fixed, weights 2^x
+      // no running maximum: x = c s - mu with mu fixed, weights 2^x (with
+      // PRESCALE the accumulators already hold x)
       (void)need_mask;
       auto weights = [&](const floatx16& sacc, int kb, uint32_t* pw) {
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c2, negmu));
+          p[r] = __builtin_amdgcn_exp2f(PRESCALE ? sacc[r] : fmaf(sacc[r], c2, negmu));
           if constexpr (MASK) p[r] = visible(kt, kb, r) ? p[r] : 0.f;
         }
         pack(p, pw);
@@ -392,7 +407,8 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     return;
   }
   const float inv = 1.f / lsum;
-  if (qvalid && lse && g == 0) lse[(size_t)bh * Nq + qrow] = kLn2 * ((FIXED ? -negmu : mrow) + log2f(lsum));
+  if constexpr (!PRESCALE)
+    if (qvalid && lse && g == 0) lse[(size_t)bh * Nq + qrow] = kLn2 * ((FIXED ? -negmu : mrow) + log2f(lsum));
   if (qvalid) {
     uint16_t* orow = O + qoff;
 #pragma unroll
@@ -442,14 +458,14 @@ transpose_v(const uint16_t* __restrict__ V, uint16_t* __restrict__ Vt, int Nk, i
   }
 }
 
-template <int D, bool FIXED, bool CAUSAL, bool PARTIAL = false, bool LAZY = false>
+template <int D, bool FIXED, bool CAUSAL, bool PARTIAL = false, bool LAZY = false, bool PRESCALE = false>
 hipError_t launch_t(const AttnArgs& a, const uint16_t* vt, int nk_pad, hipStream_t s) {
   constexpr int WAVES = FIXED ? CLIS_FIXED_WAVES : CLIS_ONLINE_WAVES;
   using G = Geo<D, WAVES>;
   const int n_qt = (a.Nq + G::BM - 1) / G::BM;
   const long long blocks = (long long)n_qt * a.n_slots;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  attn_fwd_bf16<D, FIXED, CAUSAL, WAVES, PARTIAL, LAZY><<<(unsigned)blocks, G::THREADS, 0, s>>>(
+  attn_fwd_bf16<D, FIXED, CAUSAL, WAVES, PARTIAL, LAZY, PRESCALE><<<(unsigned)blocks, G::THREADS, 0, s>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), vt, static_cast<uint16_t*>(a.o),
       a.mu, a.head_list, a.head_count, a.n_slots, a.Nq, a.Nk, nk_pad, a.c2, a.lse, a.o_acc, a.l_acc,
       a.accumulate, a.kv_offset);
@@ -462,6 +478,9 @@ hipError_t launch_d(const AttnArgs& a, bool fixed, const uint16_t* vt, int nk_pa
     if (!fixed) return hipErrorInvalidValue;
     return a.causal ? launch_t<D, true, true, true>(a, vt, nk_pad, s) : launch_t<D, true, false, true>(a, vt, nk_pad, s);
   }
+  if (fixed && !a.lse)  // output O only: pre-scaled queries
+    return a.causal ? launch_t<D, true, true, false, false, true>(a, vt, nk_pad, s)
+                    : launch_t<D, true, false, false, false, true>(a, vt, nk_pad, s);
   if (fixed) return a.causal ? launch_t<D, true, true>(a, vt, nk_pad, s) : launch_t<D, true, false>(a, vt, nk_pad, s);
   if (a.lazy)
     return a.causal ? launch_t<D, false, true, false, true>(a, vt, nk_pad, s)
