@@ -188,6 +188,8 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
   // at once, so the routing needs no host round trip.
   if (!all_online) {
     clis::AttnArgs f = a;
+    f.tail_o = at<float>(ws, L.tail_o);
+    f.tail_l = at<float>(ws, L.tail_l);
     f.mu = mu_use;
     f.head_list = lists;
     f.head_count = counts;

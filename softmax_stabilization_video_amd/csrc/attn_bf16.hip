@@ -48,6 +48,14 @@
 // disjoint key ranges simply add.  kv_offset is the global index of key 0
 // (the causal mask compares global key and query indices).
 //
+// Last-round key splits (dense fixed variant).  A grid of W workgroups runs in
+// ceil(W / P) rounds on P workgroup slots (one per CU); a partial last round of
+// T < P workgroups leaves most CUs idle.  Those T workgroups instead run as
+// S = min(8, P / T) key splits each (T*S <= P), writing fp32 unnormalized sums
+// to the workspace, and tail_combine adds the S parts and normalizes: with a
+// fixed stabilizer the parts simply add.  The split is decided on the device
+// from the routed head count, so it needs no host round trip.
+//
 // LDS layouts.  Tiles are row-major with 16-byte chunks XOR-swizzled per row,
 // so the 16 lanes that read one chunk position of 16 rows hit distinct banks.
 // The swizzle is applied when loading: lane i of a load-to-LDS instruction
@@ -57,6 +65,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "internal.h"
@@ -82,6 +91,21 @@ constexpr int kXcds = 8;                  // MI355X: workgroups are dealt round-
 constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor word 3 (untyped 32-bit data)
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLazyTau = 8.f;  // log2 units: lazy-rescale weights stay <= 256
+constexpr int kMaxSplit = 8;     // key splits per last-round workgroup
+
+// Last-round split of `active` workgroups over `conc` slots (0: none): the
+// first F run whole, the remaining T as S key splits each (S = 1: no split).
+struct TailPlan {
+  int F, T, S;
+};
+__device__ __forceinline__ TailPlan tail_plan(int active, int conc) {
+  TailPlan t{active, 0, 1};
+  if (conc <= 0) return t;
+  const int T = active % conc;
+  const int S = T > 0 ? min(kMaxSplit, conc / T) : 1;
+  if (S >= 2) t = TailPlan{active - T, T, S};
+  return t;
+}
 
 __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -149,7 +173,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const float* __restrict__ mu, const int32_t* __restrict__ head_list,
               const int32_t* __restrict__ head_count, int n_slots, int Nq, int Nk, int Nk_pad, float c2,
               float* __restrict__ lse, float* __restrict__ o_acc, float* __restrict__ l_acc, int accumulate,
-              int kv_offset_arg) {
+              int kv_offset_arg, float* __restrict__ tail_o, float* __restrict__ tail_l, int tail_conc) {
   static_assert(FIXED || !PARTIAL, "key shards use the fixed stabilizer");
   static_assert(!(FIXED && LAZY), "lazy rescaling is an online-softmax form");
   static_assert(!PRESCALE || (FIXED && !PARTIAL), "pre-scaled queries: fixed path, output O only");
@@ -158,10 +182,27 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int NS = G::NS, NC = G::NC, BM = G::BM;
   __shared__ __attribute__((aligned(1024))) char lds[2 * G::STAGE_BYTES];  // [stage][K tile, V^T tile]
 
+  constexpr bool TAIL = FIXED && !PARTIAL && !CAUSAL;  // last-round key splits
   const int n_qt = (Nq + BM - 1) / BM;
   const int active = (head_list ? *head_count : n_slots) * n_qt;
-  if ((int)blockIdx.x >= active) return;
-  const int lid = xcd_remap(blockIdx.x, active);
+  int lid, split = -1, nsplit = 1;  // split: this workgroup's slot in the tail buffers
+  if constexpr (TAIL) {
+    static_assert(BM <= kTailRows, "tail buffers hold kTailRows rows per workgroup");
+    const TailPlan tp = tail_plan(active, tail_conc);
+    const int b = blockIdx.x;
+    if (b < tp.F) {
+      lid = xcd_remap(b, tp.F);
+    } else if (b < tp.F + tp.T * tp.S) {
+      split = b - tp.F;
+      nsplit = tp.S;
+      lid = tp.F + split / tp.S;
+    } else {
+      return;
+    }
+  } else {
+    if ((int)blockIdx.x >= active) return;
+    lid = xcd_remap(blockIdx.x, active);
+  }
   const int slot = lid / n_qt;
   int qt = lid % n_qt;
   if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
@@ -178,7 +219,16 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const char* Vth = reinterpret_cast<const char*>(Vt + (size_t)bh * D * Nk_pad);
   const int vt_bytes = (D - 1) * Nk_pad * 2 + kBN * 2;  // one tile's span of V^T rows
 
-  const int kv_end = CAUSAL ? max(0, min(Nk, (qt + 1) * BM - kv_offset)) : Nk;  // local keys needed
+  // keys this workgroup covers: all of them, or its split's range of tiles
+  int nkl = Nk;
+  if (TAIL && split >= 0) {
+    const int nt = (Nk + kBN - 1) / kBN, s = split % nsplit;
+    const int t0 = s * nt / nsplit, t1 = (s + 1) * nt / nsplit;
+    Kh += (size_t)t0 * kBN * D * 2;
+    Vth += (size_t)t0 * kBN * 2;
+    nkl = max(0, min(Nk - t0 * kBN, (t1 - t0) * kBN));
+  }
+  const int kv_end = CAUSAL ? max(0, min(Nk, (qt + 1) * BM - kv_offset)) : nkl;  // local keys needed
   const int ntiles = (kv_end + kBN - 1) / kBN;
 
   // ---- per-lane, loop-invariant offsets
@@ -201,7 +251,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   for (int q = 0; q < 4; ++q) vro[q] = (uint32_t)(ln * kBN * 2 + (((2 * q + g) ^ swz_v(ln)) * 16));
 
   auto load_tile = [&](int kt, int stage) {
-    load_tiles<D, WAVES>(Kh, Vth, kt, Nk, vt_bytes, lds + stage * G::STAGE_BYTES, wave, gk, gv);
+    load_tiles<D, WAVES>(Kh, Vth, kt, nkl, vt_bytes, lds + stage * G::STAGE_BYTES, wave, gk, gv);
   };
   if (ntiles > 0) load_tile(0, 0);  // first tile in flight before anything else
 
@@ -262,7 +312,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
   auto visible = [&](int kt, int kb, int r) {
     const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-    return key < Nk && (!CAUSAL || kv_offset + key <= qrow);
+    return key < nkl && (!CAUSAL || kv_offset + key <= qrow);
   };
   // bf16 weights of one block packed for the product; the row sum adds the
   // same rounded weights
@@ -376,7 +426,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     __syncthreads();  // tile `it` is in LDS; nobody still reads the other stage
     if (it + 1 < ntiles) load_tile(kt + kBN, ST ^ 1);
     if (CAUSAL && kv_offset + kt > row0 + 31) return;  // every key of the tile is above this wave's rows
-    const bool need_mask = (kt + kBN > Nk) || (CAUSAL && kv_offset + kt + kBN - 1 > row0);
+    const bool need_mask = (kt + kBN > nkl) || (CAUSAL && kv_offset + kt + kBN - 1 > row0);
     if constexpr (FIXED) {
       // one straight-line body per mask case
       if (need_mask) tile(it, stage_tag, std::true_type{}, true);
@@ -393,6 +443,18 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // ---- epilogue: the row sum's two halves meet, then O = O_acc / l
   lsum += __shfl_xor(lsum, 32);
+  if (TAIL && split >= 0) {  // one key split: unnormalized sums for tail_combine
+    const int r = wave * 32 + ln;  // row within the workgroup
+    float* arow = tail_o + ((size_t)split * kTailRows + r) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        *reinterpret_cast<float4*>(arow + c * 32 + 8 * rq + 4 * g) =
+            make_float4(oacc[c][4 * rq], oacc[c][4 * rq + 1], oacc[c][4 * rq + 2], oacc[c][4 * rq + 3]);
+    if (g == 0) tail_l[(size_t)split * kTailRows + r] = lsum;
+    return;
+  }
   if constexpr (PARTIAL) {  // key shard: the unnormalized sums
     if (qvalid) {
       float* arow = o_acc + qoff;
@@ -420,6 +482,46 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         w.y = pack_bf16(oacc[c][4 * rq + 2] * inv, oacc[c][4 * rq + 3] * inv);
         *reinterpret_cast<uint2*>(orow + c * 32 + 8 * rq + 4 * g) = w;
       }
+  }
+}
+
+// Finishes the last round's key splits: workgroup t sums the S parts of tail
+// workgroup t in split order, then O = sum o / sum l (and the log-sum-exp when
+// asked), for the rows that exist.  256 threads: each handles 4 channels of
+// one row per pass.
+template <int D, int BM>
+__global__ void __launch_bounds__(256)
+tail_combine(const float* __restrict__ tail_o, const float* __restrict__ tail_l, uint16_t* __restrict__ O,
+             const float* __restrict__ mu, float* __restrict__ lse, const int32_t* __restrict__ head_list,
+             const int32_t* __restrict__ head_count, int n_slots, int Nq, int tail_conc) {
+  constexpr int GROUPS = D / 4, ROWS = 256 / GROUPS;  // rows per pass
+  const int n_qt = (Nq + BM - 1) / BM;
+  const int active = (head_list ? *head_count : n_slots) * n_qt;
+  const TailPlan tp = tail_plan(active, tail_conc);
+  const int t = blockIdx.x;
+  if (t >= tp.T) return;
+  const int lid = tp.F + t;
+  const int slot = lid / n_qt, qt = lid % n_qt;
+  const int bh = head_list ? head_list[slot] : slot;
+  const int cg = threadIdx.x % GROUPS, r0 = threadIdx.x / GROUPS;
+  for (int r = r0; r < BM; r += ROWS) {
+    const int qrow = qt * BM + r;
+    if (qrow >= Nq) break;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.f;
+    for (int s = 0; s < tp.S; ++s) {
+      const size_t part = (size_t)(t * tp.S + s) * kTailRows + r;
+      const float4 a = *reinterpret_cast<const float4*>(tail_o + part * D + 4 * cg);
+      acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
+      l += tail_l[part];
+    }
+    const float inv = 1.f / l;
+    const size_t row = (size_t)bh * Nq + qrow;
+    uint2 w;
+    w.x = pack_bf16(acc.x * inv, acc.y * inv);
+    w.y = pack_bf16(acc.z * inv, acc.w * inv);
+    *reinterpret_cast<uint2*>(O + row * D + 4 * cg) = w;
+    if (lse && cg == 0) lse[row] = kLn2 * (mu[row] + log2f(l));
   }
 }
 
@@ -458,17 +560,42 @@ transpose_v(const uint16_t* __restrict__ V, uint16_t* __restrict__ Vt, int Nk, i
   }
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int D, bool FIXED, bool CAUSAL, bool PARTIAL = false, bool LAZY = false, bool PRESCALE = false>
 hipError_t launch_t(const AttnArgs& a, const uint16_t* vt, int nk_pad, hipStream_t s) {
   constexpr int WAVES = FIXED ? CLIS_FIXED_WAVES : CLIS_ONLINE_WAVES;
   using G = Geo<D, WAVES>;
   const int n_qt = (a.Nq + G::BM - 1) / G::BM;
-  const long long blocks = (long long)n_qt * a.n_slots;
+  // dense fixed path: one workgroup per CU at a time; the last round's key
+  // splits need up to `conc` extra workgroups (they exit if unused)
+  const int conc = (FIXED && !PARTIAL && !CAUSAL && a.tail_o) ? min(cu_count(), kTailSlots) : 0;
+  const long long blocks = (long long)n_qt * a.n_slots + conc;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   attn_fwd_bf16<D, FIXED, CAUSAL, WAVES, PARTIAL, LAZY, PRESCALE><<<(unsigned)blocks, G::THREADS, 0, s>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), vt, static_cast<uint16_t*>(a.o),
       a.mu, a.head_list, a.head_count, a.n_slots, a.Nq, a.Nk, nk_pad, a.c2, a.lse, a.o_acc, a.l_acc,
-      a.accumulate, a.kv_offset);
+      a.accumulate, a.kv_offset, a.tail_o, a.tail_l, conc);
+  if constexpr (FIXED && !PARTIAL && !CAUSAL) {
+    if (conc > 0) {  // at most conc / 2 workgroups are split (S >= 2)
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      tail_combine<D, G::BM><<<(unsigned)(conc / 2), 256, 0, s>>>(
+          a.tail_o, a.tail_l, static_cast<uint16_t*>(a.o), a.mu, a.lse, a.head_list, a.head_count, a.n_slots,
+          a.Nq, conc);
+    }
+  }
   return hipGetLastError();
 }
 

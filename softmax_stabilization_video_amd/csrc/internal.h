@@ -37,8 +37,15 @@ struct WsLayout {
   size_t lists;      // [2][BH]     int32  heads routed fixed / online
   size_t counts;     // [2]         int32
   size_t vt;         // [BH][d][Nk_pad] bf16  V^T for the bf16 attention kernels
+  size_t tail_o;     // [kTailSlots][kTailRows][d] fp32  key-split partial sums of the last round
+  size_t tail_l;     // [kTailSlots][kTailRows]    fp32
   size_t total;
 };
+
+// Key splits of the fixed kernel's last, partial round of workgroups: at most
+// kTailSlots partial workgroups of kTailRows query rows each.
+constexpr int kTailSlots = 256;
+constexpr int kTailRows = 256;
 
 // Keys of the V^T copy, padded to whole 128-key tiles (either tile size).
 inline int vt_pad(int Nk) { return (Nk + 127) / 128 * 128; }
@@ -58,6 +65,8 @@ inline WsLayout ws_layout(int B, int H, int Nq, int Nk, int d) {
   w.lists = o;     o = align256(o + 2 * BH * sizeof(int32_t));
   w.counts = o;    o = align256(o + 2 * sizeof(int32_t));
   w.vt = o;        o = align256(o + BH * (size_t)d * vt_pad(Nk) * 2);
+  w.tail_o = o;    o = align256(o + (size_t)kTailSlots * kTailRows * d * sizeof(float));
+  w.tail_l = o;    o = align256(o + (size_t)kTailSlots * kTailRows * sizeof(float));
   w.total = o;
   return w;
 }
@@ -96,6 +105,9 @@ struct AttnArgs {
   int accumulate = 0;         // 1: add to o_acc / l_acc; 0: overwrite them
   int kv_offset = 0;          // global index of key 0 (causal mask)
   int lazy = 0;               // online path: conditional (lazy) rescaling
+  // Last-round key splits (dense fixed path): workspace for the partial sums.
+  float* tail_o = nullptr;    // [kTailSlots][kTailRows][d], or NULL: no splits
+  float* tail_l = nullptr;    // [kTailSlots][kTailRows]
 };
 
 // bf16 kernels: V is read through a transposed copy [BH][d][vt_pad(Nk)]

@@ -8,8 +8,9 @@ the oracle's B_h is not within 1e-9 (relative) of C, where the two fp64
 summation orders could disagree.
 Attention: bf16 within max abs 2e-2, mean abs 1e-3 and rel L2 5e-3 of the
 oracle; fp32 within max abs 1e-5; in every mode (fixed, online, online with
-lazy rescaling, auto).  Routing: auto mode's output for every
-head is bitwise equal to the forced mode of the route it took.
+lazy rescaling, auto).  Routing: auto mode's output for every head equals the
+forced mode of the route it took, bitwise except where the dense fixed
+kernel's last-round key splits cover other rows (then within one bf16 ulp).
 """
 import math
 
@@ -61,6 +62,21 @@ def check_certify(clis, w, host, dev, margin=1e-9):
     return mu, cert, ref
 
 
+def assert_same_kernel(a, b, exact: bool, what: str = ""):
+    """Outputs of the same kernel on the same head.  The dense fixed kernel
+    splits the keys of its last round of workgroups, and which query tiles
+    fall in that round depends on how many heads it runs: with a different
+    head count (auto mode with mixed routes against forced fixed mode) a row
+    may add its key splits in another order, which changes fp32 rounding
+    only.  Bitwise otherwise."""
+    import torch
+    if exact:
+        assert torch.equal(a, b), what
+        return
+    x, y = a.float(), b.float()
+    assert bool(((x - y).abs() <= 2.0 ** -7 * y.abs() + 1e-6).all()), what  # one bf16 ulp
+
+
 def run_attention(clis, w, host, dev, mu, cert, rows=None, modes=("fixed", "online", "online_lazy", "auto")):
     """Every mode on the device, compared with the oracle (all rows or `rows`)."""
     import torch
@@ -91,7 +107,8 @@ def run_attention(clis, w, host, dev, mu, cert, rows=None, modes=("fixed", "onli
         for b in range(w.B):
             for h in range(w.H):
                 ref = outs["fixed"] if c[b, h] else outs["online"]
-                assert torch.equal(outs["auto"][b, h], ref[b, h]), (b, h)
+                assert_same_kernel(outs["auto"][b, h], ref[b, h], exact=bool(c.all() or not c[b, h]),
+                                   what=f"{w.name} auto head {(b, h)}")
     return outs, errs
 
 
