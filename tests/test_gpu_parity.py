@@ -308,3 +308,42 @@ def test_full_size_workload(clis, name):
     import torch
     auto = outs["auto"]
     assert bool(torch.isfinite(auto).all()) and bool((auto != 0).any()), f"{name}: invalid output"
+
+
+# ---------------------------------------------------------------- maximum size
+def test_max_keys_uniform_weights(clis):
+    """The largest key count the ABI accepts at d=128 (one head's V^T just
+    under 2 GiB): with Q = 0 every score is 0, the certificate gives B_h = 0
+    and mu = 0, every weight is exactly 1, and each output row is the mean of
+    V over the keys (computed here in fp64 from the same bytes)."""
+    import torch
+    d = 128
+    nk = (0x7FFFFFFF // (2 * d)) // 128 * 128  # vt_pad(Nk) * d * 2 < 2 GiB
+    while nk * d * 2 >= 0x7FFFFFFF:
+        nk -= 128
+    nq = 300
+    say("max keys", nk, "x", d, "bf16")
+    rng = np.random.default_rng(77)
+    v_bits = np.empty((nk, d), dtype=np.uint16)
+    k_bits = np.empty((nk, d), dtype=np.uint16)
+    mean = np.zeros(d, dtype=np.float64)
+    step = 1 << 20
+    for a in range(0, nk, step):
+        b = min(nk, a + step)
+        v_bits[a:b] = workloads.round_to_bf16_bits(rng.standard_normal((b - a, d), dtype=np.float32))
+        k_bits[a:b] = workloads.round_to_bf16_bits(rng.standard_normal((b - a, d), dtype=np.float32))
+        mean += workloads.bf16_bits_to_f32(v_bits[a:b]).astype(np.float64).sum(axis=0)
+    mean /= nk
+    q = torch.zeros((1, 1, nq, d), dtype=torch.bfloat16, device="cuda")
+    k = workloads.to_torch(k_bits.reshape(1, 1, nk, d), "bf16")
+    v = workloads.to_torch(v_bits.reshape(1, 1, nk, d), "bf16")
+    del k_bits, v_bits
+    mu, cert, stats, _ = clis.clis_certify(q, k, v, 1.0 / math.sqrt(d), want_stats=True)
+    o = clis.clis_attn_fwd(q, k, v, 1.0 / math.sqrt(d), mode="auto", mu=mu, cert=cert)
+    torch.cuda.synchronize()
+    st = clis.decode_stats(stats)[0]
+    assert int(cert.item()) == 1 and st["bound"] == 0.0 and st["L"] == math.ceil(math.log2(nk))
+    assert not mu.any()
+    got = to_f64(o)[0, 0]
+    # fp32 sums of exact weights, then one bf16 rounding of |mean| < 1e-2
+    np.testing.assert_allclose(got, np.broadcast_to(mean, got.shape), rtol=0, atol=2e-5)
