@@ -141,17 +141,19 @@ def cpu_baseline(w, Q, K, V, budget_s: float):
         sample[(b, h)] = (rows, ref)
         total_rows += len(rows)
         flops += float(np.sum([4.0 * w.d * ((r + 1) if w.causal else w.Nk) for r in rows]))
-    # certification of one head, timed the same way
-    q, k, v = head_inputs(*heads[0])
-    t0 = time.perf_counter()
-    oracle.certify_head(q, k, v, w.scale, p_bf16=(w.dtype == "bf16"))
-    t_cert = time.perf_counter() - t0
-    full_s = t_total * (w.B * w.H * w.Nq) / total_rows + t_cert * len(heads)
+    # certification of every head (linear in N, so all of it fits the budget)
+    t_cert = 0.0
+    for b, h in heads:
+        q, k, v = head_inputs(b, h)
+        t0 = time.perf_counter()
+        oracle.certify_head(q, k, v, w.scale, p_bf16=(w.dtype == "bf16"))
+        t_cert += time.perf_counter() - t0
+    full_s = t_total * (w.B * w.H * w.Nq) / total_rows + t_cert
     rec = {
         "value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": f"fp64 softmax attention of {total_rows} seeded query rows ({per_head} per head, all "
-                  f"{len(heads)} heads) against all {w.Nk} keys; certification of 1 head timed separately",
-        "sample_seconds": round(t_total, 3), "certify_one_head_s": round(t_cert, 3),
+                  f"{len(heads)} heads) against all {w.Nk} keys; certification of all heads timed separately",
+        "sample_seconds": round(t_total, 3), "certify_all_heads_s": round(t_cert, 3),
         "extrapolated_full_call_s": round(full_s, 1),
     }
     return rec, sample
@@ -349,6 +351,8 @@ def main(argv=None):
                    "heads_certified": n_cert, "heads": w.B * w.H},
         "pct_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
         "step_ms_median_events": round(statistics.median(step_events), 4),
+        "step_ms_min_events": round(min(step_events), 4),
+        "step_ms_mean_events": round(statistics.mean(step_events), 4),
     }
     if "clis_kernel_ms" in res:
         out["clis_kernel_tflops"] = round(flops / res["clis_kernel_ms"] / 1e9, 2)
