@@ -63,7 +63,7 @@ T* at(void* ws, size_t off) {
 // Enqueue certification into caller buffers (workspace for the partials).
 int do_certify(const void* q, const void* k, const void* v, int B, int H, int Nq, int Nk, int d,
                float scale, int dtype, float* mu, int32_t* cert, clis_head_stats_t* stats,
-               double* kbar, void* ws, hipStream_t s) {
+               double* kbar, void* ws, hipStream_t s, const float* vmax_blk = nullptr) {
   const clis::WsLayout L = clis::ws_layout(B, H, Nq, Nk, d);
   clis::CertifyArgs a{};
   a.q = q; a.k = k; a.v = v;
@@ -78,6 +78,8 @@ int do_certify(const void* q, const void* k, const void* v, int B, int H, int Nq
   a.vmax_part = at<double>(ws, L.vmax_part);
   a.kap_part = at<double>(ws, L.kap_part);
   a.qss_part = at<double>(ws, L.qss_part);
+  a.vmax_blk = vmax_blk;
+  a.vmax_nblk = clis::vt_pad(Nk) / 64;
   const hipError_t e = clis::launch_certify(a, s);
   if (e != hipSuccess) return hip_fail(e, "certify launch");
   return CLIS_OK;
@@ -157,24 +159,27 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
   }
   const clis::WsLayout L = clis::ws_layout(B, H, Nq, Nk, d);
   const int BH = B * H;
+  const bool need_cert = (mode == CLIS_MODE_AUTO && (!cert || !mu)) || (mode == CLIS_MODE_FIXED && !mu);
   hipError_t e;
   void* vt = nullptr;
+  float* vmax_blk = nullptr;  // the transpose also takes certification's max |V|
   if (needs_vt(dtype)) {
     vt = at<void>(ws, L.vt);
-    if ((e = clis::launch_transpose_v(v, vt, BH, Nk, d, s)) != hipSuccess) return hip_fail(e, "V transpose launch");
+    if (need_cert) vmax_blk = at<float>(ws, L.vmax_blk);
+    if ((e = clis::launch_transpose_v(v, vt, BH, Nk, d, s, vmax_blk)) != hipSuccess)
+      return hip_fail(e, "V transpose launch");
   }
   if (plain_online) {
     e = launch_attn(a, dtype, false, vt, s);
     return e == hipSuccess ? CLIS_OK : hip_fail(e, "online attention launch");
   }
 
-  const bool need_cert = (mode == CLIS_MODE_AUTO && (!cert || !mu)) || (mode == CLIS_MODE_FIXED && !mu);
   const float* mu_use = mu;
   const int32_t* cert_use = cert;
   if (need_cert) {
     float* mu_ws = at<float>(ws, L.mu);
     int32_t* cert_ws = at<int32_t>(ws, L.cert);
-    st = do_certify(q, k, v, B, H, Nq, Nk, d, scale, dtype, mu_ws, cert_ws, nullptr, nullptr, ws, s);
+    st = do_certify(q, k, v, B, H, Nq, Nk, d, scale, dtype, mu_ws, cert_ws, nullptr, nullptr, ws, s, vmax_blk);
     if (st != CLIS_OK) return st;
     mu_use = mu_ws;
     cert_use = cert_ws;

@@ -528,26 +528,51 @@ tail_combine(const float* __restrict__ tail_o, const float* __restrict__ tail_l,
 // V [BH][Nk][D] -> V^T [BH][D][Nk_pad], keys permuted within 16-key groups
 // (vt_pos), zeros past the last key.  One block transposes 64 keys x D
 // channels through LDS: coalesced 16-byte reads along channels, coalesced
-// 16-byte writes along keys.
+// 16-byte writes along keys.  With vmax_blk set it also writes the block's
+// max |V| (NaN kept), so certification need not read V again.
 template <int D>
 __global__ void __launch_bounds__(256)
-transpose_v(const uint16_t* __restrict__ V, uint16_t* __restrict__ Vt, int Nk, int Nk_pad) {
+transpose_v(const uint16_t* __restrict__ V, uint16_t* __restrict__ Vt, int Nk, int Nk_pad,
+            float* __restrict__ vmax_blk) {
   constexpr int TK = 64;               // keys per block
   __shared__ uint16_t t[D][TK + 2];    // [channel][key position]; +2 breaks bank strides
   const int bh = blockIdx.y, kt = blockIdx.x * TK;
   const uint16_t* src = V + (size_t)bh * Nk * D;
   uint16_t* dst = Vt + (size_t)bh * D * Nk_pad;
   constexpr int CPR = D / 8;
+  float vmax = 0.f;
   for (int i = threadIdx.x; i < TK * CPR; i += 256) {
     const int r = i / CPR, ch = i % CPR, key = kt + r;
     uint4 u = make_uint4(0, 0, 0, 0);
     if (key < Nk) u = *reinterpret_cast<const uint4*>(src + (size_t)key * D + ch * 8);
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    if (vmax_blk) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float((w[e] & 0x7fffu) << 16), hi = __uint_as_float(w[e] & 0x7fff0000u);
+        vmax = (lo > vmax || lo != lo) ? lo : vmax;
+        vmax = (hi > vmax || hi != hi) ? hi : vmax;
+      }
+    }
     const int pos = vt_pos(r);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       t[ch * 8 + 2 * e][pos] = (uint16_t)(w[e] & 0xffffu);
       t[ch * 8 + 2 * e + 1][pos] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  if (vmax_blk) {  // the block's max |V|: waves, then the four wave results
+    __shared__ float red[4];
+    for (int off = 32; off > 0; off >>= 1) {
+      const float o = __shfl_xor(vmax, off);
+      vmax = (o > vmax || o != o) ? o : vmax;
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = vmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float m = red[0];
+      for (int i = 1; i < 4; ++i) m = (red[i] > m || red[i] != red[i]) ? red[i] : m;
+      vmax_blk[(size_t)bh * gridDim.x + blockIdx.x] = m;
     }
   }
   __syncthreads();
@@ -617,10 +642,12 @@ hipError_t launch_d(const AttnArgs& a, bool fixed, const uint16_t* vt, int nk_pa
 
 }  // namespace
 
-hipError_t launch_transpose_v(const void* v, void* vt, int BH, int Nk, int d, hipStream_t s) {
+hipError_t launch_transpose_v(const void* v, void* vt, int BH, int Nk, int d, hipStream_t s, float* vmax_blk) {
   const dim3 grid((unsigned)(vt_pad(Nk) / 64), (unsigned)BH);
-  if (d == 128) transpose_v<128><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), static_cast<uint16_t*>(vt), Nk, vt_pad(Nk));
-  else if (d == 64) transpose_v<64><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), static_cast<uint16_t*>(vt), Nk, vt_pad(Nk));
+  const uint16_t* src = static_cast<const uint16_t*>(v);
+  uint16_t* dst = static_cast<uint16_t*>(vt);
+  if (d == 128) transpose_v<128><<<grid, 256, 0, s>>>(src, dst, Nk, vt_pad(Nk), vmax_blk);
+  else if (d == 64) transpose_v<64><<<grid, 256, 0, s>>>(src, dst, Nk, vt_pad(Nk), vmax_blk);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

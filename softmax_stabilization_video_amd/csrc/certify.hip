@@ -10,6 +10,9 @@
 //   1. cert_keys_values: per (head, key split) partial column sums of K and
 //      partial max |V|                                   (steps 1 and 5)
 //   2. cert_kbar: kbar = (sum of partials in split order) / Nk      (step 1)
+//      (when the bf16 attention path has already transposed V, that pass
+//      wrote max |V| per 64-key block; cert_keys_values then skips V and
+//      cert_kbar folds the block maxima into the first split's partial)
 //   3. cert_norms: key splits -> partial max ||k - kbar||^2 (steps 2-3);
 //      query splits -> partial max ||q||^2 and mu_r = c (q_r . kbar)
 //   4. cert_finalize: kappa, B_h, G, A, C, flag per head         (steps 3-7)
@@ -93,7 +96,7 @@ cert_keys_values(const T* __restrict__ K, const T* __restrict__ V, int Nk, int S
   split_range(Nk, Sk, split, &lo, &hi);
   const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
   const T* kb = K + (size_t)bh * Nk * D;
-  const T* vb = V + (size_t)bh * Nk * D;
+  const T* vb = V ? V + (size_t)bh * Nk * D : nullptr;  // NULL: max |V| comes from the transpose
   double acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
@@ -103,9 +106,11 @@ cert_keys_values(const T* __restrict__ K, const T* __restrict__ V, int Nk, int S
     load_vec(kb + (size_t)j * D + tc * VEC, x);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] += x[e];
-    load_vec(vb + (size_t)j * D + tc * VEC, x);
+    if (vb) {
+      load_vec(vb + (size_t)j * D + tc * VEC, x);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) vmax = max_keep_nan(vmax, fabs(x[e]));
+      for (int e = 0; e < VEC; ++e) vmax = max_keep_nan(vmax, fabs(x[e]));
+    }
   }
 #pragma unroll
   for (int e = 0; e < VEC; ++e) colsum[tr][tc * VEC + e] = acc[e];
@@ -122,8 +127,22 @@ cert_keys_values(const T* __restrict__ K, const T* __restrict__ V, int Nk, int S
 // Step 1: kbar from the split partials, summed in split order.
 template <int D>
 __global__ void __launch_bounds__(D)
-cert_kbar(const double* __restrict__ ksum_part, int Nk, int Sk, double* __restrict__ kbar) {
+cert_kbar(const double* __restrict__ ksum_part, int Nk, int Sk, double* __restrict__ kbar,
+          const float* __restrict__ vmax_blk, int nblk, double* __restrict__ vmax_part) {
   const int bh = blockIdx.x, c = threadIdx.x;
+  if (vmax_blk) {  // block maxima of |V| from the transpose -> split 0's partial
+    __shared__ double red[(D + 63) / 64];
+    double m = 0.0;
+    for (int i = c; i < nblk; i += D) m = max_keep_nan(m, (double)vmax_blk[(size_t)bh * nblk + i]);
+    for (int off = 32; off > 0; off >>= 1) m = max_keep_nan(m, __shfl_xor(m, off));
+    if ((c & 63) == 0) red[c >> 6] = m;
+    __syncthreads();
+    if (c == 0) {
+      double r = red[0];
+      for (int w = 1; w < (D + 63) / 64; ++w) r = max_keep_nan(r, red[w]);
+      vmax_part[(size_t)bh * Sk] = r;
+    }
+  }
   const double* p = ksum_part + (size_t)bh * Sk * D + c;
   double s = 0.0;
   for (int i = 0; i < Sk; ++i) s += p[(size_t)i * D];
@@ -288,8 +307,9 @@ hipError_t certify_typed(const CertifyArgs& a, hipStream_t s) {
   const T* q = static_cast<const T*>(a.q);
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
-  cert_keys_values<T, D><<<dim3(Sk, BH), kThreads, 0, s>>>(k, v, a.Nk, Sk, a.ksum_part, a.vmax_part);
-  cert_kbar<D><<<BH, D, 0, s>>>(a.ksum_part, a.Nk, Sk, a.kbar);
+  cert_keys_values<T, D><<<dim3(Sk, BH), kThreads, 0, s>>>(k, a.vmax_blk ? nullptr : v, a.Nk, Sk, a.ksum_part,
+                                                             a.vmax_part);
+  cert_kbar<D><<<BH, D, 0, s>>>(a.ksum_part, a.Nk, Sk, a.kbar, a.vmax_blk, a.vmax_nblk, a.vmax_part);
   cert_norms<T, D><<<dim3(Sk + Sq, BH), kThreads, 0, s>>>(q, k, a.kbar, a.Nq, a.Nk, Sk, Sq, c2, a.mu,
                                                           a.kap_part, a.qss_part);
   const int fb = (BH + kThreads - 1) / kThreads;

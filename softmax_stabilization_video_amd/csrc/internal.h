@@ -37,6 +37,7 @@ struct WsLayout {
   size_t lists;      // [2][BH]     int32  heads routed fixed / online
   size_t counts;     // [2]         int32
   size_t vt;         // [BH][d][Nk_pad] bf16  V^T for the bf16 attention kernels
+  size_t vmax_blk;   // [BH][vt_pad(Nk) / 64] fp32  max |V| per 64-key block, from the V transpose
   size_t tail_o;     // [kTailSlots][kTailRows][d] fp32  key-split partial sums of the last round
   size_t tail_l;     // [kTailSlots][kTailRows]    fp32
   size_t total;
@@ -65,6 +66,7 @@ inline WsLayout ws_layout(int B, int H, int Nq, int Nk, int d) {
   w.lists = o;     o = align256(o + 2 * BH * sizeof(int32_t));
   w.counts = o;    o = align256(o + 2 * sizeof(int32_t));
   w.vt = o;        o = align256(o + BH * (size_t)d * vt_pad(Nk) * 2);
+  w.vmax_blk = o;  o = align256(o + BH * (size_t)(vt_pad(Nk) / 64) * sizeof(float));
   w.tail_o = o;    o = align256(o + (size_t)kTailSlots * kTailRows * d * sizeof(float));
   w.tail_l = o;    o = align256(o + (size_t)kTailSlots * kTailRows * sizeof(float));
   w.total = o;
@@ -81,6 +83,10 @@ struct CertifyArgs {
   clis_head_stats_t* stats;  // [BH] (never NULL here: workspace copy if the caller gave none)
   double* kbar;              // [BH][d]
   double* ksum_part; double* vmax_part; double* kap_part; double* qss_part;
+  // If set: max |V| per 64-key block, already computed by the V transpose
+  // (vmax_nblk blocks per head); certification then does not read V.
+  const float* vmax_blk = nullptr;
+  int vmax_nblk = 0;
 };
 
 hipError_t launch_certify(const CertifyArgs& a, hipStream_t s);
@@ -112,7 +118,9 @@ struct AttnArgs {
 
 // bf16 kernels: V is read through a transposed copy [BH][d][vt_pad(Nk)]
 // that launch_transpose_v writes.
-hipError_t launch_transpose_v(const void* v, void* vt, int BH, int Nk, int d, hipStream_t s);
+// vmax_blk (or NULL): also writes max |V| of every 64-key block, [BH][vt_pad(Nk) / 64].
+hipError_t launch_transpose_v(const void* v, void* vt, int BH, int Nk, int d, hipStream_t s,
+                              float* vmax_blk = nullptr);
 hipError_t launch_attn_bf16(const AttnArgs& a, bool fixed, const void* vt, hipStream_t s);
 hipError_t launch_attn_fp32(const AttnArgs& a, bool fixed, hipStream_t s);
 

@@ -223,6 +223,29 @@ def test_non_finite_input_never_certifies(clis):
         assert_close(got[0, h], want[0, h], "bf16", f"nan/head{h}")
 
 
+def test_certification_inside_the_call_matches_clis_certify(clis):
+    """Auto mode without a certificate certifies inside the call, taking max |V|
+    from the V transpose pass instead of reading V again: its routes equal
+    clis_certify's flags and the oracle's, with NaN, +Inf, the largest finite
+    bf16 and a large ordinary value planted in V."""
+    import torch
+    w = workloads.custom("vmax", 1, 5, 300, 128, "bf16", False)
+    (Q, K, V), _ = _inputs(w, seed=13)
+    V = V.copy()
+    V[0, 1, 7, 3] = 0x7FC0      # NaN
+    V[0, 2, 250, 100] = 0x7F80  # +Inf
+    V[0, 3, 0, 0] = 0xFF7F      # -3.39e38: G = 128
+    V[0, 4, 299, 127] = workloads.round_to_bf16_bits(np.array([1000.0], dtype=np.float32))[0]
+    dev = tuple(to_device(a, w.dtype) for a in (Q, K, V))
+    mu, cert = clis.clis_certify(*dev, w.scale)
+    _, route = clis.clis_attn_fwd(*dev, w.scale, mode="auto", want_route=True)
+    torch.cuda.synchronize()
+    ref = oracle.certify(Q, K, V, w.dtype, w.scale)["cert"]
+    assert ref.tolist() == [[1, 0, 0, 0, 1]]
+    assert np.array_equal(cert.cpu().numpy(), ref)
+    assert np.array_equal(route.cpu().numpy(), ref)
+
+
 def test_certified_head_near_the_cap_stays_finite(clis):
     """A head whose bound sits just under C, with one query aligned to one
     outlying key so the largest exp2 argument nearly reaches the bound."""
