@@ -16,10 +16,12 @@
  * Stabilizers mu [B, H, Nq] fp32, flags cert and routes [B, H] int32.
  *
  * Ownership.  The caller owns every buffer.  All pointers except `stream`
- * are DEVICE pointers; q, k, v, o must be 16-byte aligned and ws 256-byte
- * aligned.  The library never allocates or frees memory; scratch space comes
- * from the caller's workspace `ws` of at least clis_workspace_bytes(...)
- * bytes.  `stream` is a hipStream_t passed as void* (NULL: the null stream).
+ * are DEVICE pointers; q, k, v, o, o_acc must be 16-byte aligned, ws
+ * 256-byte aligned, stats and kbar 8-byte aligned, and the other fp32 and
+ * int32 arrays 4-byte aligned.  The library never allocates or frees memory;
+ * scratch space comes from the caller's workspace `ws` of at least
+ * clis_workspace_bytes(...) bytes.  `stream` is a hipStream_t passed as void*
+ * (NULL: the null stream).
  *
  * Execution.  Every call only enqueues kernels on `stream` and returns; there
  * is no host synchronisation and no device-to-host copy, also in auto mode,
@@ -69,7 +71,7 @@ typedef enum {
   CLIS_ERR_NULL = 1,        /* a required pointer is NULL */
   CLIS_ERR_SHAPE = 2,       /* bad dimension, scale, or causal with Nq != Nk */
   CLIS_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, or unknown dtype / mode */
-  CLIS_ERR_ALIGN = 4,       /* q/k/v/o not 16-byte, or ws not 256-byte aligned */
+  CLIS_ERR_ALIGN = 4,       /* a pointer below its alignment (see Ownership) */
   CLIS_ERR_WORKSPACE = 5,   /* ws missing or smaller than clis_workspace_bytes() */
   CLIS_ERR_HIP = 6          /* a HIP launch failed; see clis_last_error() */
 } clis_status_t;
@@ -88,9 +90,13 @@ typedef struct {
   int32_t reserved;
 } clis_head_stats_t;
 
-/* Workspace bytes any entry point of this library needs for these shapes
- * (the certification scratch, stabilizers, flags, route lists, and a
- * transposed copy of V for the bf16 attention kernels). */
+/* Workspace bytes any entry point of this library needs for these shapes, a
+ * pure function of them (256 if any is <= 0):
+ *   - certification scratch, stabilizers, flags and route lists (small);
+ *   - a transposed copy of V for the bf16 attention kernels (about the size
+ *     of V, keys rounded up to 128) and its max |V| per 64 keys;
+ *   - fp32 partial sums for the fixed kernel's last-round key splits:
+ *     256 x 256 rows x (d + 1) floats, about 32 MiB at d = 128. */
 size_t clis_workspace_bytes(int B, int H, int Nq, int Nk, int d);
 
 /*

@@ -8,7 +8,8 @@ without a built library raises.
 
 Entry points (same names as the C ABI):
     clis_certify(q, k, v, scale)       -> (mu, cert[, stats, kbar])
-    clis_attn_fwd(q, k, v, ...)        -> o            (mode auto/fixed/online)
+    clis_attn_fwd(q, k, v, ...)        -> o[, route][, lse]
+                                          (mode auto/fixed/online/online_lazy)
     online_attn_fwd(q, k, v, ...)      -> o            (optionally with lse)
     clis_attn_fwd_partial(q, k_shard, v_shard, mu, o_acc, l_acc, ...)
     clis_attn_combine(o_acc, l_acc, ...) -> o        (optionally with lse)

@@ -130,6 +130,8 @@ int clis_certify(const void* q, const void* k, const void* v, int B, int H, int 
   if (st != CLIS_OK || empty) return st;
   if ((st = check_io(q, k, v, nullptr, false)) != CLIS_OK) return st;
   if (!mu_out || !cert_out) return fail(CLIS_ERR_NULL, "mu_out and cert_out must be non-NULL");
+  if (!aligned(mu_out, 4) || !aligned(cert_out, 4) || !aligned(stats_out, 8) || !aligned(kbar_out, 8))
+    return fail(CLIS_ERR_ALIGN, "mu_out and cert_out must be 4-byte, stats_out and kbar_out 8-byte aligned");
   if ((st = check_ws(ws, ws_bytes, B, H, Nq, Nk, d)) != CLIS_OK) return st;
   return do_certify(q, k, v, B, H, Nq, Nk, d, scale, dtype, mu_out, cert_out, stats_out, kbar_out, ws,
                     static_cast<hipStream_t>(stream));
@@ -148,7 +150,9 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
   int st = check_common(B, H, Nq, Nk, d, scale, dtype, causal, &empty);
   if (st != CLIS_OK || empty) return st;
   if ((st = check_io(q, k, v, o, true)) != CLIS_OK) return st;
-  if (lse_out && !aligned(lse_out, 4)) return fail(CLIS_ERR_ALIGN, "lse_out must be 4-byte aligned");
+  if ((lse_out && !aligned(lse_out, 4)) || (mu && !aligned(mu, 4)) || (cert && !aligned(cert, 4)) ||
+      (route_out && !aligned(route_out, 4)))
+    return fail(CLIS_ERR_ALIGN, "mu, cert, route_out and lse_out must be 4-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   clis::AttnArgs a = attn_args(q, k, v, o, B, H, Nq, Nk, d, scale, causal);
   a.lse = lse_out;

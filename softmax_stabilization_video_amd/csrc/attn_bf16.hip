@@ -1,5 +1,5 @@
-// attn_bf16.hip -- fused attention forward on gfx950 bf16 MFMA, in two
-// variants from one template:
+// attn_bf16.hip -- fused attention forward on gfx950 bf16 MFMA.  One kernel
+// template covers three softmax forms:
 //   FIXED  -- CLiS: each query row's stabilizer mu_i is fixed before the key
 //             loop, so the loop has no running maximum, no cross-lane step
 //             and no accumulator rescaling ("CLiS: Plug-and-Play Attention
@@ -13,8 +13,13 @@
 //             stabilizer in use moves, and the accumulators are rescaled, only
 //             when a row's tile maximum exceeds it by more than kLazyTau (log2
 //             units), under a wave-uniform branch; weights stay <= 2^kLazyTau.
-// The two variants use independently tuned workgroup sizes (the pages tune
-// tiles per method too, Table 7 caption).
+// The fixed form has three more switches: PARTIAL (key shards: fp32
+// unnormalized sums in and out), PRESCALE (when only O is wanted, the query
+// fragments are pre-multiplied by c and the score products start from -mu, so
+// a weight is one exp2 of the accumulator), and, for the dense non-shard
+// form, the last-round key splits below.  The fixed and online forms use
+// independently tuned workgroup sizes (the pages tune tiles per method too,
+// Table 7 caption).
 //
 // Work decomposition.  A workgroup of WAVES waves owns 32*WAVES query rows of
 // one (batch, head); each wave owns 32 rows, and two waves share a SIMD.  K
@@ -42,10 +47,13 @@
 //
 // Outputs.  Normally O = O_acc / l in bf16, and optionally each row's
 // log-sum-exp ln 2 * (m + log2 l), where m is the fixed mu_i or the final
-// running maximum (both in log2 units).  With o_acc set (fixed variant only,
-// for key-value shards) the kernel instead starts from, or overwrites, fp32
-// unnormalized sums o_acc and l_acc: with a fixed stabilizer the sums over
-// disjoint key ranges simply add.  kv_offset is the global index of key 0
+// running maximum (both in log2 units).  The log-sum-exp comes from the fixed
+// form without PRESCALE: rounding c q to bf16 (error e) shifts every score of
+// a row by the common term e.kbar plus a small key-dependent part, and the
+// common term cancels in O but not in ln l.  With o_acc set (fixed variant
+// only, for key-value shards) the kernel instead starts from, or overwrites,
+// fp32 unnormalized sums o_acc and l_acc: with a fixed stabilizer the sums
+// over disjoint key ranges simply add.  kv_offset is the global index of key 0
 // (the causal mask compares global key and query indices).
 //
 // Last-round key splits (dense fixed variant).  A grid of W workgroups runs in

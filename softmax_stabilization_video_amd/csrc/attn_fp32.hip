@@ -1,10 +1,12 @@
-// attn_fp32.hip -- fp32 attention forward (fixed-stabilizer and online
-// variants) for fp32 inputs, where the result must stay within fp32 accuracy
-// of softmax attention.  bf16 MFMA would round the operands, so this path
-// runs fp32 FMAs on the VALU; it serves small fp32 problems, not the
-// throughput workloads.  Same two variants as the bf16 kernel ("CLiS:
-// Plug-and-Play Attention Acceleration for Video Diffusion on TPUs via
-// Certified Stabilization", abstract and Figure 5(a)).
+// attn_fp32.hip -- fp32 attention forward for fp32 inputs, where the result
+// must stay within fp32 accuracy of softmax attention.  bf16 MFMA would round
+// the operands, so this path runs fp32 FMAs on the VALU; it serves small fp32
+// problems, not the throughput workloads.  The softmax forms are those of the
+// bf16 kernel ("CLiS: Plug-and-Play Attention Acceleration for Video
+// Diffusion on TPUs via Certified Stabilization", abstract and Figure 5(a)):
+// fixed stabilizer (with its key-shard form, o_acc / l_acc), online softmax,
+// and online softmax with lazy rescaling; each can also write the row
+// log-sum-exp.
 //
 // One workgroup = 64 threads = 64 query rows of one head; each thread owns a
 // row (its output accumulator in registers, its query row in LDS).  Key and

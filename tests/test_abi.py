@@ -76,15 +76,18 @@ def _fake(addr=0x10000):
     (dict(ws=None, mode=0), 5),          # auto mode needs a workspace
     (dict(ws_bytes=10, mode=0), 5),
     (dict(lse=0x60002), 4),              # lse_out not 4-byte aligned
+    (dict(mu=0x70002), 4),               # fp32 / int32 arrays need 4-byte alignment
+    (dict(cert=0x70001), 4),
+    (dict(route=0x70003), 4),
 ])
 def test_argument_checks_reject_before_launch(clis, case, expected):
     a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, B=1, H=2, Nq=10, Nk=10, d=64, scale=0.125,
-             causal=0, dtype=0, mode=1, ws=0x50000, ws_bytes=1 << 30, lse=None)
+             causal=0, dtype=0, mode=1, ws=0x50000, ws_bytes=1 << 30, lse=None, mu=None, cert=None, route=None)
     a.update(case)
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
     st = clis.lib.clis_attn_fwd(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), a["B"], a["H"], a["Nq"],
-                                a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], a["mode"], None, None,
-                                None, vp(a["lse"]), vp(a["ws"]), a["ws_bytes"], None)
+                                a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], a["mode"], vp(a["mu"]),
+                                vp(a["cert"]), vp(a["route"]), vp(a["lse"]), vp(a["ws"]), a["ws_bytes"], None)
     assert st == expected, clis.lib.clis_last_error()
     assert clis.lib.clis_last_error() != b""
 
@@ -145,6 +148,19 @@ def test_certify_requires_outputs(clis):
     st = clis.lib.clis_certify(_fake(), _fake(), _fake(), 1, 1, 8, 8, 64, 0.1, 0, None, None, None, None,
                                _fake(0x1000000), 1 << 30, None)
     assert st == 1
+
+
+@pytest.mark.parametrize("mu,cert,stats,kbar", [
+    (0x40002, 0x50000, None, None),
+    (0x40000, 0x50002, None, None),
+    (0x40000, 0x50000, 0x60004, None),   # clis_head_stats_t and fp64 outputs need 8 bytes
+    (0x40000, 0x50000, None, 0x60004),
+])
+def test_certify_rejects_misaligned_outputs(clis, mu, cert, stats, kbar):
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = clis.lib.clis_certify(_fake(), _fake(), _fake(), 1, 1, 8, 8, 64, 0.1, 0, vp(mu), vp(cert), vp(stats),
+                               vp(kbar), _fake(0x1000000), 1 << 30, None)
+    assert st == 4, clis.lib.clis_last_error()
 
 
 def test_product_path_never_touches_the_oracle():
