@@ -93,6 +93,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef CLIS_ONLINE_WAVES
 #define CLIS_ONLINE_WAVES 4
 #endif
+#ifndef CLIS_FIXED_CAUSAL_WAVES
+#define CLIS_FIXED_CAUSAL_WAVES CLIS_FIXED_WAVES
+#endif
 
 constexpr int kBN = 64;                   // keys per tile
 constexpr int kXcds = 8;                  // MI355X: workgroups are dealt round-robin to 8 XCDs
@@ -433,7 +436,6 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // tile `it` is in LDS; nobody still reads the other stage
     if (it + 1 < ntiles) load_tile(kt + kBN, ST ^ 1);
-    if (CAUSAL && kv_offset + kt > row0 + 31) return;  // every key of the tile is above this wave's rows
     const bool need_mask = (kt + kBN > nkl) || (CAUSAL && kv_offset + kt + kBN - 1 > row0);
     if constexpr (FIXED) {
       // one straight-line body per mask case
@@ -444,9 +446,26 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
-  for (int it = 0; it < ntiles; it += 2) {
+  // Tiles this wave computes.  Under the causal mask the last ones of the
+  // workgroup can lie wholly above this wave's rows; the wave still takes part
+  // in their barriers and loads, in a loop of its own after the compute loop
+  // (a skip inside the compute loop makes hipcc copy the output accumulators
+  // at every tile).
+  int nt_wave = ntiles;
+  if constexpr (CAUSAL) {
+    const int x = row0 + 32 - kv_offset;  // local keys up to this wave's last row, plus one
+    nt_wave = x <= 0 ? 0 : min(ntiles, (x + kBN - 1) / kBN);
+  }
+  for (int it = 0; it < nt_wave; it += 2) {
     step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
+    if (it + 1 < nt_wave) step(it + 1, std::integral_constant<int, 1>{});
+  }
+  if constexpr (CAUSAL) {
+    for (int it = nt_wave; it < ntiles; ++it) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (it + 1 < ntiles) load_tile((it + 1) * kBN, (it + 1) & 1);
+    }
   }
 
   // ---- epilogue: the row sum's two halves meet, then O = O_acc / l
@@ -608,7 +627,7 @@ int cu_count() {
 
 template <int D, bool FIXED, bool CAUSAL, bool PARTIAL = false, bool LAZY = false, bool PRESCALE = false>
 hipError_t launch_t(const AttnArgs& a, const uint16_t* vt, int nk_pad, hipStream_t s) {
-  constexpr int WAVES = FIXED ? CLIS_FIXED_WAVES : CLIS_ONLINE_WAVES;
+  constexpr int WAVES = FIXED ? (CAUSAL ? CLIS_FIXED_CAUSAL_WAVES : CLIS_FIXED_WAVES) : CLIS_ONLINE_WAVES;
   using G = Geo<D, WAVES>;
   const int n_qt = (a.Nq + G::BM - 1) / G::BM;
   // dense fixed path: one workgroup per CU at a time; the last round's key
