@@ -93,6 +93,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef CLIS_ONLINE_WAVES
 #define CLIS_ONLINE_WAVES 4
 #endif
+#ifndef CLIS_CAUSAL_GROUP
+#define CLIS_CAUSAL_GROUP 2
+#endif
 #ifndef CLIS_FIXED_CAUSAL_WAVES
 #define CLIS_FIXED_CAUSAL_WAVES CLIS_FIXED_WAVES
 #endif
@@ -214,9 +217,26 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if ((int)blockIdx.x >= active) return;
     lid = xcd_remap(blockIdx.x, active);
   }
-  const int slot = lid / n_qt;
-  int qt = lid % n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
+  int slot, qt;
+  if constexpr (CAUSAL) {
+    // Longest query tiles first, with heads taken in groups of G.  An XCD
+    // deals consecutive workgroups round-robin to its four shader engines and
+    // waits, in order, for a free CU in the next one, so every four
+    // consecutive workgroups should be of (nearly) equal length and each
+    // engine's total work equal: the G heads of a group advance together,
+    // through their query tiles in blocks of M = 4 / G, every other block in
+    // reverse.
+    constexpr int G = CLIS_CAUSAL_GROUP, M = 4 / G;
+    static_assert(G == 1 || G == 2 || G == 4, "heads per group: 1, 2 or 4");
+    const int heads = active / n_qt, grp = lid / (G * n_qt);
+    const int width = min(G, heads - G * grp), r = lid - G * n_qt * grp;
+    slot = G * grp + r % width;
+    const int p = r / width, blk = p / M, e = p % M, top = n_qt - 1 - M * blk;
+    qt = (blk % 2 == 1 && blk < n_qt / M) ? top - (M - 1) + e : top - e;
+  } else {
+    slot = lid / n_qt;
+    qt = lid % n_qt;
+  }
   const int bh = head_list ? head_list[slot] : slot;
 
   const int tid = threadIdx.x, lane = tid & 63;

@@ -129,6 +129,9 @@ SMALL = [
     ("bf16_exact_tiles", 1, 1, 256, 256, 128, "bf16", False),
     ("bf16_causal_tail", 1, 3, 777, 777, 128, "bf16", True),
     ("bf16_causal_d64", 2, 1, 300, 300, 64, "bf16", True),
+    # causal work order: an odd head count (a partial group of heads) and an
+    # odd number of 256-row query tiles (a partial block of tiles)
+    ("bf16_causal_odd_groups", 1, 5, 1200, 1200, 128, "bf16", True),
     ("bf16_cross", 2, 1, 300, 1300, 128, "bf16", False),
     ("bf16_lt_tile", 1, 1, 5, 5, 128, "bf16", False),
     ("bf16_one_key", 1, 2, 70, 1, 128, "bf16", False),
