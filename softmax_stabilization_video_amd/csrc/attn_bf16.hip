@@ -56,13 +56,17 @@
 // over disjoint key ranges simply add.  kv_offset is the global index of key 0
 // (the causal mask compares global key and query indices).
 //
-// Last-round key splits (dense fixed variant).  A grid of W workgroups runs in
-// ceil(W / P) rounds on P workgroup slots (one per CU); a partial last round of
-// T < P workgroups leaves most CUs idle.  Those T workgroups instead run as
-// S = min(8, P / T) key splits each (T*S <= P), writing fp32 unnormalized sums
-// to the workspace, and tail_combine adds the S parts and normalizes: with a
-// fixed stabilizer the parts simply add.  The split is decided on the device
-// from the routed head count, so it needs no host round trip.
+// Work pool (dense fixed variant).  A grid of W workgroups runs in rounds of
+// P (one per CU), and the XCDs of one GPU run at different clocks under this
+// load, so with the hardware's fixed round-robin deal of workgroups to XCDs
+// the slowest XCD finishes last, and a partial last round leaves most CUs
+// idle.  The last tenth of the items (at least the partial round) is instead
+// a pool claimed from a device counter by the workgroups that follow the
+// others: first whole items, then items cut into 8 key splits that write fp32
+// unnormalized sums to the workspace, added in split order and normalized by
+// tail_combine (with a fixed stabilizer the parts simply add).  XCDs that run
+// faster reach the pool earlier and claim more of it.  The counter is zeroed
+// by the route kernel that precedes every launch.
 //
 // LDS layouts.  Tiles are row-major with 16-byte chunks XOR-swizzled per row,
 // so the 16 lanes that read one chunk position of 16 rows hit distinct banks.
@@ -73,6 +77,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -105,19 +110,34 @@ constexpr int kXcds = 8;                  // MI355X: workgroups are dealt round-
 constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor word 3 (untyped 32-bit data)
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLazyTau = 8.f;  // log2 units: lazy-rescale weights stay <= 256
-constexpr int kMaxSplit = 8;     // key splits per last-round workgroup
+constexpr int kMaxSplit = 8;     // key splits per pool item
+#ifndef CLIS_POOL_DIV
+#define CLIS_POOL_DIV 10         // pool: at least 1 / CLIS_POOL_DIV of the items (0: the last round only)
+#endif
+#ifndef CLIS_POOL_OVER
+#define CLIS_POOL_OVER 50        // pool workgroups launched beyond one per claim, in percent
+#endif
 
-// Last-round split of `active` workgroups over `conc` slots (0: none): the
-// first F run whole, the remaining T as S key splits each (S = 1: no split).
-struct TailPlan {
-  int F, T, S;
+// Work of the dense fixed form: `active` items (query tiles of the routed
+// heads).  The first F run one workgroup each, in XCD-local order.  The last
+// P form a pool: its first P1 items whole, then P2 items as kMaxSplit key
+// splits each (fp32 partial sums in the tail buffers, added in split order by
+// tail_combine).  The workgroups after the first F each claim one pool entry
+// (a whole item or a split) from a device counter when they start, and exit
+// if none is left.  There are more of them than entries, and an XCD reaches
+// its share of them once its own items are under way, so XCDs that run faster
+// (the XCDs of one GPU run at different clocks under load) claim more of the
+// pool; the splits at its end even out the last round.
+struct PoolPlan {
+  int F, P1, P2;
 };
-__device__ __forceinline__ TailPlan tail_plan(int active, int conc) {
-  TailPlan t{active, 0, 1};
-  if (conc <= 0) return t;
-  const int T = active % conc;
-  const int S = T > 0 ? min(kMaxSplit, conc / T) : 1;
-  if (S >= 2) t = TailPlan{active - T, T, S};
+__host__ __device__ inline PoolPlan pool_plan(int active, int conc) {
+  PoolPlan t{active, 0, 0};
+  if (conc <= 0 || active <= 0) return t;
+  int P = max(active % conc, CLIS_POOL_DIV > 0 ? active / CLIS_POOL_DIV : 0);
+  P = min(P, active);
+  const int P2 = min(P, kTailSlots / kMaxSplit);
+  t = PoolPlan{active - P, P - P2, P2};
   return t;
 }
 
@@ -187,7 +207,8 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const float* __restrict__ mu, const int32_t* __restrict__ head_list,
               const int32_t* __restrict__ head_count, int n_slots, int Nq, int Nk, int Nk_pad, float c2,
               float* __restrict__ lse, float* __restrict__ o_acc, float* __restrict__ l_acc, int accumulate,
-              int kv_offset_arg, float* __restrict__ tail_o, float* __restrict__ tail_l, int tail_conc) {
+              int kv_offset_arg, float* __restrict__ tail_o, float* __restrict__ tail_l, int tail_conc,
+              int* __restrict__ sched) {
   static_assert(FIXED || !PARTIAL, "key shards use the fixed stabilizer");
   static_assert(!(FIXED && LAZY), "lazy rescaling is an online-softmax form");
   static_assert(!PRESCALE || (FIXED && !PARTIAL), "pre-scaled queries: fixed path, output O only");
@@ -202,16 +223,27 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   int lid, split = -1, nsplit = 1;  // split: this workgroup's slot in the tail buffers
   if constexpr (TAIL) {
     static_assert(BM <= kTailRows, "tail buffers hold kTailRows rows per workgroup");
-    const TailPlan tp = tail_plan(active, tail_conc);
+    const PoolPlan pp = pool_plan(active, tail_conc);
     const int b = blockIdx.x;
-    if (b < tp.F) {
-      lid = xcd_remap(b, tp.F);
-    } else if (b < tp.F + tp.T * tp.S) {
-      split = b - tp.F;
-      nsplit = tp.S;
-      lid = tp.F + split / tp.S;
-    } else {
-      return;
+    if (b < pp.F) {
+      lid = xcd_remap(b, pp.F);
+    } else {  // pool workgroup: claim one entry
+      // broadcast through LDS stage 1, which the second tile's load first
+      // writes after a barrier every wave reaches past this read (a separate
+      // LDS variable makes hipcc wait for each tile load before the next
+      // product)
+      int* claim = reinterpret_cast<int*>(lds + G::STAGE_BYTES);
+      if (threadIdx.x == 0) *claim = atomicAdd(sched, 1);
+      __syncthreads();
+      const int c = *claim;
+      if (c < pp.P1) {  // a whole item
+        lid = pp.F + c;
+      } else {
+        split = c - pp.P1;  // a key split: its slot in the tail buffers
+        if (split >= pp.P2 * kMaxSplit) return;
+        nsplit = kMaxSplit;
+        lid = pp.F + pp.P1 + split / kMaxSplit;
+      }
     }
   } else {
     if ((int)blockIdx.x >= active) return;
@@ -532,10 +564,10 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
-// Finishes the last round's key splits: workgroup t sums the S parts of tail
-// workgroup t in split order, then O = sum o / sum l (and the log-sum-exp when
-// asked), for the rows that exist.  256 threads: each handles 4 channels of
-// one row per pass.
+// Finishes the pool's key splits: workgroup t sums the kMaxSplit parts of the
+// t-th split item in split order, then O = sum o / sum l (and the log-sum-exp
+// when asked), for the rows that exist.  256 threads: each handles 4 channels
+// of one row per pass.
 template <int D, int BM>
 __global__ void __launch_bounds__(256)
 tail_combine(const float* __restrict__ tail_o, const float* __restrict__ tail_l, uint16_t* __restrict__ O,
@@ -544,10 +576,10 @@ tail_combine(const float* __restrict__ tail_o, const float* __restrict__ tail_l,
   constexpr int GROUPS = D / 4, ROWS = 256 / GROUPS;  // rows per pass
   const int n_qt = (Nq + BM - 1) / BM;
   const int active = (head_list ? *head_count : n_slots) * n_qt;
-  const TailPlan tp = tail_plan(active, tail_conc);
+  const PoolPlan pp = pool_plan(active, tail_conc);
   const int t = blockIdx.x;
-  if (t >= tp.T) return;
-  const int lid = tp.F + t;
+  if (t >= pp.P2) return;
+  const int lid = pp.F + pp.P1 + t;
   const int slot = lid / n_qt, qt = lid % n_qt;
   const int bh = head_list ? head_list[slot] : slot;
   const int cg = threadIdx.x % GROUPS, r0 = threadIdx.x / GROUPS;
@@ -556,8 +588,8 @@ tail_combine(const float* __restrict__ tail_o, const float* __restrict__ tail_l,
     if (qrow >= Nq) break;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float l = 0.f;
-    for (int s = 0; s < tp.S; ++s) {
-      const size_t part = (size_t)(t * tp.S + s) * kTailRows + r;
+    for (int s = 0; s < kMaxSplit; ++s) {
+      const size_t part = (size_t)(t * kMaxSplit + s) * kTailRows + r;
       const float4 a = *reinterpret_cast<const float4*>(tail_o + part * D + 4 * cg);
       acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
       l += tail_l[part];
@@ -650,20 +682,34 @@ hipError_t launch_t(const AttnArgs& a, const uint16_t* vt, int nk_pad, hipStream
   constexpr int WAVES = FIXED ? (CAUSAL ? CLIS_FIXED_CAUSAL_WAVES : CLIS_FIXED_WAVES) : CLIS_ONLINE_WAVES;
   using G = Geo<D, WAVES>;
   const int n_qt = (a.Nq + G::BM - 1) / G::BM;
-  // dense fixed path: one workgroup per CU at a time; the last round's key
-  // splits need up to `conc` extra workgroups (they exit if unused)
-  const int conc = (FIXED && !PARTIAL && !CAUSAL && a.tail_o) ? min(cu_count(), kTailSlots) : 0;
-  const long long blocks = (long long)n_qt * a.n_slots + conc;
+  // dense fixed path: one workgroup per CU at a time (conc of them); the
+  // pool's workgroups follow the whole items (they exit once it is empty)
+  const int conc = (FIXED && !PARTIAL && !CAUSAL && a.tail_o && a.sched) ? min(cu_count(), kPoolWorkers) : 0;
+  long long blocks = (long long)n_qt * a.n_slots;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (conc > 0) {
+    // Pool workgroups.  The device routes active <= blocks items; the
+    // blocks - F >= P1 + P2 workgroups past its F claim too, and it has
+    // P1 + P2 * kMaxSplit entries, so (kMaxSplit - 1) * P2 extra workgroups
+    // suffice for any active, with P <= pmax = min(blocks, max(conc - 1,
+    // blocks / CLIS_POOL_DIV)) and P2 <= min(pmax, kTailSlots / kMaxSplit).
+    // CLIS_POOL_OVER percent more of every entry's worth lets faster XCDs
+    // claim more.
+    const long long div = CLIS_POOL_DIV > 0 ? blocks / CLIS_POOL_DIV : 0;
+    const long long pmax = std::min<long long>(blocks, std::max<long long>(conc - 1, div));
+    const long long p2max = std::min<long long>(pmax, kTailSlots / kMaxSplit);
+    blocks += (kMaxSplit - 1) * p2max + (pmax + (kMaxSplit - 1) * p2max) * CLIS_POOL_OVER / 100;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  }
   attn_fwd_bf16<D, FIXED, CAUSAL, WAVES, PARTIAL, LAZY, PRESCALE><<<(unsigned)blocks, G::THREADS, 0, s>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), vt, static_cast<uint16_t*>(a.o),
       a.mu, a.head_list, a.head_count, a.n_slots, a.Nq, a.Nk, nk_pad, a.c2, a.lse, a.o_acc, a.l_acc,
-      a.accumulate, a.kv_offset, a.tail_o, a.tail_l, conc);
+      a.accumulate, a.kv_offset, a.tail_o, a.tail_l, conc, a.sched);
   if constexpr (FIXED && !PARTIAL && !CAUSAL) {
-    if (conc > 0) {  // at most conc / 2 workgroups are split (S >= 2)
+    if (conc > 0) {  // one workgroup per possible pool item
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      tail_combine<D, G::BM><<<(unsigned)(conc / 2), 256, 0, s>>>(
+      tail_combine<D, G::BM><<<(unsigned)(kTailSlots / kMaxSplit), 256, 0, s>>>(
           a.tail_o, a.tail_l, static_cast<uint16_t*>(a.o), a.mu, a.lse, a.head_list, a.head_count, a.n_slots,
           a.Nq, conc);
     }

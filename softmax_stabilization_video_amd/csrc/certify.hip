@@ -296,6 +296,8 @@ route_heads(const int32_t* __restrict__ cert, int mode, int BH, int32_t* __restr
   if (lane == 0) {
     counts[0] = nf;
     counts[1] = no;
+    counts[2] = 0;  // work counters of the attention kernels that follow
+    counts[3] = 0;
   }
 }
 
