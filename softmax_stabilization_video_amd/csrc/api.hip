@@ -157,7 +157,9 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
   clis::AttnArgs a = attn_args(q, k, v, o, B, H, Nq, Nk, d, scale, causal);
   a.lse = lse_out;
   a.lazy = (mode == CLIS_MODE_ONLINE_LAZY);
-  const bool plain_online = (all_online && !route_out);
+  // fp32 online needs no workspace: one kernel; every bf16 call routes first
+  // (the route kernel also zeroes the kernels' work counters)
+  const bool plain_online = (all_online && !route_out && !needs_vt(dtype));
   if (!plain_online || needs_vt(dtype)) {
     if ((st = check_ws(ws, ws_bytes, B, H, Nq, Nk, d)) != CLIS_OK) return st;
   }
@@ -209,6 +211,7 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
     clis::AttnArgs g = a;
     g.head_list = lists + BH;
     g.head_count = counts + 1;
+    g.sched = counts + 3;  // zeroed by the route kernel above
     if ((e = launch_attn(g, dtype, false, vt, s)) != hipSuccess) return hip_fail(e, "online attention launch");
   }
   return CLIS_OK;

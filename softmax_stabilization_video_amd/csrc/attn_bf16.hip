@@ -56,17 +56,18 @@
 // over disjoint key ranges simply add.  kv_offset is the global index of key 0
 // (the causal mask compares global key and query indices).
 //
-// Work pool (dense fixed variant).  A grid of W workgroups runs in rounds of
-// P (one per CU), and the XCDs of one GPU run at different clocks under this
-// load, so with the hardware's fixed round-robin deal of workgroups to XCDs
-// the slowest XCD finishes last, and a partial last round leaves most CUs
-// idle.  The last tenth of the items (at least the partial round) is instead
-// a pool claimed from a device counter by the workgroups that follow the
-// others: first whole items, then items cut into 8 key splits that write fp32
-// unnormalized sums to the workspace, added in split order and normalized by
-// tail_combine (with a fixed stabilizer the parts simply add).  XCDs that run
-// faster reach the pool earlier and claim more of it.  The counter is zeroed
-// by the route kernel that precedes every launch.
+// Work pool (dense forms).  A grid of W workgroups runs in rounds of the
+// workgroups resident at once, and the XCDs of one GPU run at different clocks
+// under this load, so with the hardware's fixed round-robin deal of
+// workgroups to XCDs the slowest XCD finishes last, and a partial last round
+// leaves most CUs idle.  The last tenth of the items (at least the partial
+// round) is instead a pool claimed from a device counter by the workgroups
+// that follow the others: whole items, and in the fixed form then items cut
+// into 8 key splits that write fp32 unnormalized sums to the workspace, added
+// in split order and normalized by tail_combine (with a fixed stabilizer the
+// parts simply add).  XCDs that run faster reach the pool earlier and claim
+// more of it.  The counters are zeroed by the route kernel that precedes
+// every launch.
 //
 // LDS layouts.  Tiles are row-major with 16-byte chunks XOR-swizzled per row,
 // so the 16 lanes that read one chunk position of 16 rows hit distinct banks.
@@ -131,12 +132,12 @@ constexpr int kMaxSplit = 8;     // key splits per pool item
 struct PoolPlan {
   int F, P1, P2;
 };
-__host__ __device__ inline PoolPlan pool_plan(int active, int conc) {
+__host__ __device__ inline PoolPlan pool_plan(int active, int conc, bool splits) {
   PoolPlan t{active, 0, 0};
   if (conc <= 0 || active <= 0) return t;
   int P = max(active % conc, CLIS_POOL_DIV > 0 ? active / CLIS_POOL_DIV : 0);
   P = min(P, active);
-  const int P2 = min(P, kTailSlots / kMaxSplit);
+  const int P2 = splits ? min(P, kTailSlots / kMaxSplit) : 0;
   t = PoolPlan{active - P, P - P2, P2};
   return t;
 }
@@ -207,7 +208,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const float* __restrict__ mu, const int32_t* __restrict__ head_list,
               const int32_t* __restrict__ head_count, int n_slots, int Nq, int Nk, int Nk_pad, float c2,
               float* __restrict__ lse, float* __restrict__ o_acc, float* __restrict__ l_acc, int accumulate,
-              int kv_offset_arg, float* __restrict__ tail_o, float* __restrict__ tail_l, int tail_conc,
+              int kv_offset_arg, float* __restrict__ tail_o, float* __restrict__ tail_l, int pool_conc,
               int* __restrict__ sched) {
   static_assert(FIXED || !PARTIAL, "key shards use the fixed stabilizer");
   static_assert(!(FIXED && LAZY), "lazy rescaling is an online-softmax form");
@@ -221,9 +222,9 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int n_qt = (Nq + BM - 1) / BM;
   const int active = (head_list ? *head_count : n_slots) * n_qt;
   int lid, split = -1, nsplit = 1;  // split: this workgroup's slot in the tail buffers
-  if constexpr (TAIL) {
-    static_assert(BM <= kTailRows, "tail buffers hold kTailRows rows per workgroup");
-    const PoolPlan pp = pool_plan(active, tail_conc);
+  static_assert(!TAIL || BM <= kTailRows, "tail buffers hold kTailRows rows per workgroup");
+  if (!PARTIAL && !CAUSAL && sched) {  // pooled work (file comment)
+    const PoolPlan pp = pool_plan(active, pool_conc, TAIL && tail_o);
     const int b = blockIdx.x;
     if (b < pp.F) {
       lid = xcd_remap(b, pp.F);
@@ -240,7 +241,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         lid = pp.F + c;
       } else {
         split = c - pp.P1;  // a key split: its slot in the tail buffers
-        if (split >= pp.P2 * kMaxSplit) return;
+        if (!TAIL || split >= pp.P2 * kMaxSplit) return;
         nsplit = kMaxSplit;
         lid = pp.F + pp.P1 + split / kMaxSplit;
       }
@@ -572,11 +573,11 @@ template <int D, int BM>
 __global__ void __launch_bounds__(256)
 tail_combine(const float* __restrict__ tail_o, const float* __restrict__ tail_l, uint16_t* __restrict__ O,
              const float* __restrict__ mu, float* __restrict__ lse, const int32_t* __restrict__ head_list,
-             const int32_t* __restrict__ head_count, int n_slots, int Nq, int tail_conc) {
+             const int32_t* __restrict__ head_count, int n_slots, int Nq, int pool_conc) {
   constexpr int GROUPS = D / 4, ROWS = 256 / GROUPS;  // rows per pass
   const int n_qt = (Nq + BM - 1) / BM;
   const int active = (head_list ? *head_count : n_slots) * n_qt;
-  const PoolPlan pp = pool_plan(active, tail_conc);
+  const PoolPlan pp = pool_plan(active, pool_conc, true);
   const int t = blockIdx.x;
   if (t >= pp.P2) return;
   const int lid = pp.F + pp.P1 + t;
@@ -682,9 +683,13 @@ hipError_t launch_t(const AttnArgs& a, const uint16_t* vt, int nk_pad, hipStream
   constexpr int WAVES = FIXED ? (CAUSAL ? CLIS_FIXED_CAUSAL_WAVES : CLIS_FIXED_WAVES) : CLIS_ONLINE_WAVES;
   using G = Geo<D, WAVES>;
   const int n_qt = (a.Nq + G::BM - 1) / G::BM;
-  // dense fixed path: one workgroup per CU at a time (conc of them); the
-  // pool's workgroups follow the whole items (they exit once it is empty)
-  const int conc = (FIXED && !PARTIAL && !CAUSAL && a.tail_o && a.sched) ? min(cu_count(), kPoolWorkers) : 0;
+  // pooled work of the dense forms (file comment): conc workgroups are
+  // resident at a time; the pool's workgroups follow the others and exit once
+  // it is empty.  The causal forms keep their static order: claims from all
+  // XCDs interleave and would undo its balance across shader engines.
+  constexpr bool TAIL = FIXED && !PARTIAL && !CAUSAL;
+  const bool splits = TAIL && a.tail_o;
+  const int conc = (!PARTIAL && !CAUSAL && a.sched) ? min(cu_count(), kPoolWorkers) * (WAVES >= 8 ? 1 : 2) : 0;
   long long blocks = (long long)n_qt * a.n_slots;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (conc > 0) {
@@ -697,16 +702,16 @@ hipError_t launch_t(const AttnArgs& a, const uint16_t* vt, int nk_pad, hipStream
     // claim more.
     const long long div = CLIS_POOL_DIV > 0 ? blocks / CLIS_POOL_DIV : 0;
     const long long pmax = std::min<long long>(blocks, std::max<long long>(conc - 1, div));
-    const long long p2max = std::min<long long>(pmax, kTailSlots / kMaxSplit);
+    const long long p2max = splits ? std::min<long long>(pmax, kTailSlots / kMaxSplit) : 0;
     blocks += (kMaxSplit - 1) * p2max + (pmax + (kMaxSplit - 1) * p2max) * CLIS_POOL_OVER / 100;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   }
   attn_fwd_bf16<D, FIXED, CAUSAL, WAVES, PARTIAL, LAZY, PRESCALE><<<(unsigned)blocks, G::THREADS, 0, s>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), vt, static_cast<uint16_t*>(a.o),
       a.mu, a.head_list, a.head_count, a.n_slots, a.Nq, a.Nk, nk_pad, a.c2, a.lse, a.o_acc, a.l_acc,
-      a.accumulate, a.kv_offset, a.tail_o, a.tail_l, conc, a.sched);
-  if constexpr (FIXED && !PARTIAL && !CAUSAL) {
-    if (conc > 0) {  // one workgroup per possible pool item
+      a.accumulate, a.kv_offset, a.tail_o, a.tail_l, conc, conc > 0 ? a.sched : nullptr);
+  if constexpr (TAIL) {
+    if (conc > 0 && splits) {  // one workgroup per possible split item
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       tail_combine<D, G::BM><<<(unsigned)(kTailSlots / kMaxSplit), 256, 0, s>>>(

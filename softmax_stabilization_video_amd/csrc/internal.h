@@ -117,7 +117,7 @@ struct AttnArgs {
   // Last-round key splits (dense fixed path): workspace for the partial sums.
   float* tail_o = nullptr;    // [kTailSlots][kTailRows][d], or NULL: no splits
   float* tail_l = nullptr;    // [kTailSlots][kTailRows]
-  int* sched = nullptr;       // pool counter, zero at launch (required with tail_o)
+  int* sched = nullptr;       // pool counter, zero at launch, or NULL: no pool
 };
 
 // bf16 kernels: V is read through a transposed copy [BH][d][vt_pad(Nk)]
