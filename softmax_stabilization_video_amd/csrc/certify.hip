@@ -43,10 +43,12 @@ __device__ __forceinline__ double to_f64(uint16_t b) {
 }
 __device__ __forceinline__ double to_f64(float f) { return (double)f; }
 
+// Rows in flight per lane in the streaming loops (loads issued before use).
+constexpr int kUnroll = 4;
+
 // 16 bytes of row elements, widened to fp64.
 template <typename T>
-__device__ __forceinline__ void load_vec(const T* p, double* out) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ void widen(const uint4 u, double* out) {
   if constexpr (sizeof(T) == 2) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -101,15 +103,31 @@ cert_keys_values(const T* __restrict__ K, const T* __restrict__ V, int Nk, int S
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
   double vmax = 0.0;
-  for (int j = lo + tr; j < hi; j += RPI) {
-    double x[VEC];
-    load_vec(kb + (size_t)j * D + tc * VEC, x);
+  // kUnroll rows per lane in flight; the sums still run in row order
+  for (int j0 = lo + tr; j0 < hi; j0 += kUnroll * RPI) {
+    uint4 uk[kUnroll], uv[kUnroll];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] += x[e];
-    if (vb) {
-      load_vec(vb + (size_t)j * D + tc * VEC, x);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int j = j0 + u * RPI;
+      uk[u] = make_uint4(0, 0, 0, 0);
+      uv[u] = make_uint4(0, 0, 0, 0);
+      if (j < hi) {
+        uk[u] = *reinterpret_cast<const uint4*>(kb + (size_t)j * D + tc * VEC);
+        if (vb) uv[u] = *reinterpret_cast<const uint4*>(vb + (size_t)j * D + tc * VEC);
+      }
+    }
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) vmax = max_keep_nan(vmax, fabs(x[e]));
+    for (int u = 0; u < kUnroll; ++u) {
+      if (j0 + u * RPI >= hi) break;
+      double x[VEC];
+      widen<T>(uk[u], x);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += x[e];
+      if (vb) {
+        widen<T>(uv[u], x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) vmax = max_keep_nan(vmax, fabs(x[e]));
+      }
     }
   }
 #pragma unroll
@@ -178,20 +196,29 @@ cert_norms(const T* __restrict__ Q, const T* __restrict__ K, const double* __res
     const T* base = K + (size_t)bh * Nk * D;
     // every lane of a row group runs the same trip count, so the shuffles
     // inside row_sum always see their partners
-    for (int j0 = lo; j0 < hi; j0 += RPI) {
-      const int j = j0 + tr;
-      double ss = 0.0;
-      if (j < hi) {
-        double x[VEC];
-        load_vec(base + (size_t)j * D + tc * VEC, x);
+    for (int j0 = lo; j0 < hi; j0 += kUnroll * RPI) {
+      uint4 uk[kUnroll];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const double t = x[e] - kb[e];
-          ss += t * t;
-        }
+      for (int u = 0; u < kUnroll; ++u) {
+        const int j = j0 + u * RPI + tr;
+        uk[u] = j < hi ? *reinterpret_cast<const uint4*>(base + (size_t)j * D + tc * VEC) : make_uint4(0, 0, 0, 0);
       }
-      ss = row_sum<TPR>(ss);
-      if (j < hi) best = max_keep_nan(best, ss);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int j = j0 + u * RPI + tr;
+        double ss = 0.0;
+        if (j < hi) {
+          double x[VEC];
+          widen<T>(uk[u], x);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const double t = x[e] - kb[e];
+            ss += t * t;
+          }
+        }
+        ss = row_sum<TPR>(ss);
+        if (j < hi) best = max_keep_nan(best, ss);
+      }
     }
     best = block_max(best, red);
     if (threadIdx.x == 0) kap_part[(size_t)bh * Sk + split] = best;
@@ -200,23 +227,32 @@ cert_norms(const T* __restrict__ Q, const T* __restrict__ K, const double* __res
     int lo, hi;
     split_range(Nq, Sq, split, &lo, &hi);
     const T* base = Q + (size_t)bh * Nq * D;
-    for (int r0 = lo; r0 < hi; r0 += RPI) {
-      const int r = r0 + tr;
-      double ss = 0.0, dot = 0.0;
-      if (r < hi) {
-        double x[VEC];
-        load_vec(base + (size_t)r * D + tc * VEC, x);
+    for (int r0 = lo; r0 < hi; r0 += kUnroll * RPI) {
+      uint4 uq[kUnroll];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          ss += x[e] * x[e];
-          dot += x[e] * kb[e];
-        }
+      for (int u = 0; u < kUnroll; ++u) {
+        const int r = r0 + u * RPI + tr;
+        uq[u] = r < hi ? *reinterpret_cast<const uint4*>(base + (size_t)r * D + tc * VEC) : make_uint4(0, 0, 0, 0);
       }
-      ss = row_sum<TPR>(ss);
-      dot = row_sum<TPR>(dot);
-      if (r < hi) {
-        best = max_keep_nan(best, ss);
-        if (tc == 0) mu[(size_t)bh * Nq + r] = (float)(c2 * dot);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int r = r0 + u * RPI + tr;
+        double ss = 0.0, dot = 0.0;
+        if (r < hi) {
+          double x[VEC];
+          widen<T>(uq[u], x);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            ss += x[e] * x[e];
+            dot += x[e] * kb[e];
+          }
+        }
+        ss = row_sum<TPR>(ss);
+        dot = row_sum<TPR>(dot);
+        if (r < hi) {
+          best = max_keep_nan(best, ss);
+          if (tc == 0) mu[(size_t)bh * Nq + r] = (float)(c2 * dot);
+        }
       }
     }
     best = block_max(best, red);
