@@ -64,8 +64,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.online_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, vp, sz, vp]
     L.clis_attn_fwd_partial.argtypes = [vp, vp, vp, i, i, i, i, i, f, i, i, vp, i, i, vp, vp, vp, sz, vp]
     L.clis_attn_combine.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, vp]
-    for fn in (L.clis_certify, L.clis_attn_fwd, L.online_attn_fwd, L.clis_abi_version):
+    for fn in (L.clis_certify, L.clis_attn_fwd, L.online_attn_fwd, L.clis_attn_fwd_partial, L.clis_attn_combine,
+               L.clis_abi_version):
         fn.restype = ctypes.c_int
+    L.clis_abi_version.argtypes = []
     L.clis_status_string.argtypes = [i]
     L.clis_status_string.restype = ctypes.c_char_p
     L.clis_last_error.argtypes = []
@@ -233,9 +235,16 @@ def clis_attn_combine(o_acc, l_acc, dtype=None, mu=None, want_lse: bool = False,
     want_lse also each row's log-sum-exp ln 2 (mu + log2 l).  Returns o, or
     (o, lse)."""
     import torch
+    if o_acc.dim() != 4:
+        raise ValueError("o_acc must be [B, H, Nq, d]")
     B, H, Nq, d = o_acc.shape
+    for t, shape in ((o_acc, (B, H, Nq, d)), (l_acc, (B, H, Nq))) + (((mu, (B, H, Nq)),) if mu is not None else ()):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"o_acc, l_acc and mu must be contiguous fp32 GPU tensors; expected shape {shape}")
     dtype = torch.bfloat16 if dtype is None else dtype
     o = torch.empty((B, H, Nq, d), dtype=dtype, device=o_acc.device) if out is None else out
+    if tuple(o.shape) != (B, H, Nq, d) or not o.is_contiguous():
+        raise ValueError(f"out must be contiguous with shape {(B, H, Nq, d)}")
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=o_acc.device) if want_lse else None
     code = CLIS_BF16 if o.dtype == torch.bfloat16 else CLIS_FP32 if o.dtype == torch.float32 else None
     if code is None:
