@@ -125,7 +125,8 @@ constexpr int kMaxSplit = 8;     // key splits per pool item
 // splits each (fp32 partial sums in the tail buffers, added in split order by
 // tail_combine).  The workgroups after the first F each claim one pool entry
 // (a whole item or a split) from a device counter when they start, and exit
-// if none is left.  There are more of them than entries, and an XCD reaches
+// if none is left (or at once when the pool is empty, e.g. when no head is
+// routed to the kernel).  There are more of them than entries, and an XCD reaches
 // its share of them once its own items are under way, so XCDs that run faster
 // (the XCDs of one GPU run at different clocks under load) claim more of the
 // pool; the splits at its end even out the last round.
@@ -229,12 +230,19 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (b < pp.F) {
       lid = xcd_remap(b, pp.F);
     } else {  // pool workgroup: claim one entry
+      const int entries = pp.P1 + pp.P2 * kMaxSplit;
+      if (entries == 0) return;  // nothing pooled (no head routed to this kernel)
       // broadcast through LDS stage 1, which the second tile's load first
       // writes after a barrier every wave reaches past this read (a separate
       // LDS variable makes hipcc wait for each tile load before the next
-      // product)
+      // product).  The counter only grows, so once a plain read shows the
+      // pool drained the claim is skipped: it would fail, and thousands of
+      // claims on one address cost more than the reads.
       int* claim = reinterpret_cast<int*>(lds + G::STAGE_BYTES);
-      if (threadIdx.x == 0) *claim = atomicAdd(sched, 1);
+      if (threadIdx.x == 0) {
+        const int seen = __hip_atomic_load(sched, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *claim = seen < entries ? atomicAdd(sched, 1) : seen;
+      }
       __syncthreads();
       const int c = *claim;
       if (c < pp.P1) {  // a whole item
