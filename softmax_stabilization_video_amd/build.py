@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libclis.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "certify.hip", "attn_bf16.hip", "attn_fp32.hip", "combine.hip"]
+SOURCES = ["api.hip", "certify.hip", "transpose.hip", "attn_bf16.hip", "attn_fp32.hip", "combine.hip"]
 PROBE_SOURCES = ["probe_mfma.hip"]
 PROBE_LIB = os.path.join(HERE, "libclis_probe.so")
 ARCH = "gfx950"

@@ -38,12 +38,12 @@
 // lane l^32 only for the online tile maximum and the final row sum.
 //
 // V^T.  The P.V operand needs, per lane, eight keys of one channel: keys
-// 4g..4g+3 and 8+4g..8+4g+3 of a 16-key step.  transpose_v writes V^T per
-// head as [d][Nk_pad] with each 16-key group stored as {0-3, 8-11, 4-7,
-// 12-15}, which makes those eight keys contiguous, so one ds_read_b128 fetches
-// an operand (instead of two LDS transpose reads from a row-major V tile; on
-// gfx950 the LDS read issue rate bounds a 32-row MFMA attention).  Nk_pad is a
-// multiple of 128; keys past Nk are zero.
+// 4g..4g+3 and 8+4g..8+4g+3 of a 16-key step.  transpose_v (transpose.hip)
+// writes V^T per head as [d][Nk_pad] with each 16-key group stored as {0-3,
+// 8-11, 4-7, 12-15}, which makes those eight keys contiguous, so one
+// ds_read_b128 fetches an operand (instead of two LDS transpose reads from a
+// row-major V tile; on gfx950 the LDS read issue rate bounds a 32-row MFMA
+// attention).  Nk_pad is a multiple of 128; keys past Nk are zero.
 //
 // Outputs.  Normally O = O_acc / l in bf16, and optionally each row's
 // log-sum-exp ln 2 * (m + log2 l), where m is the fixed mu_i or the final
@@ -160,9 +160,6 @@ __device__ __forceinline__ int xcd_remap(int bid, int active) {
   const int base = active / kXcds, rem = active % kXcds;
   return (x < rem) ? x * (base + 1) + i : rem * (base + 1) + (x - rem) * base + i;
 }
-
-// Position of key k within its 16-key group in V^T: swap bits 2 and 3.
-__device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 template <int D, int WAVES>
 struct Geo {
@@ -613,66 +610,6 @@ tail_combine(const float* __restrict__ tail_o, const float* __restrict__ tail_l,
   }
 }
 
-// V [BH][Nk][D] -> V^T [BH][D][Nk_pad], keys permuted within 16-key groups
-// (vt_pos), zeros past the last key.  One block transposes 64 keys x D
-// channels through LDS: coalesced 16-byte reads along channels, coalesced
-// 16-byte writes along keys.  With vmax_blk set it also writes the block's
-// max |V| (NaN kept), so certification need not read V again.
-template <int D>
-__global__ void __launch_bounds__(256)
-transpose_v(const uint16_t* __restrict__ V, uint16_t* __restrict__ Vt, int Nk, int Nk_pad,
-            float* __restrict__ vmax_blk) {
-  constexpr int TK = 64;               // keys per block
-  __shared__ uint16_t t[D][TK + 2];    // [channel][key position]; +2 breaks bank strides
-  const int bh = blockIdx.y, kt = blockIdx.x * TK;
-  const uint16_t* src = V + (size_t)bh * Nk * D;
-  uint16_t* dst = Vt + (size_t)bh * D * Nk_pad;
-  constexpr int CPR = D / 8;
-  float vmax = 0.f;
-  for (int i = threadIdx.x; i < TK * CPR; i += 256) {
-    const int r = i / CPR, ch = i % CPR, key = kt + r;
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (key < Nk) u = *reinterpret_cast<const uint4*>(src + (size_t)key * D + ch * 8);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-    if (vmax_blk) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = __uint_as_float((w[e] & 0x7fffu) << 16), hi = __uint_as_float(w[e] & 0x7fff0000u);
-        vmax = (lo > vmax || lo != lo) ? lo : vmax;
-        vmax = (hi > vmax || hi != hi) ? hi : vmax;
-      }
-    }
-    const int pos = vt_pos(r);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      t[ch * 8 + 2 * e][pos] = (uint16_t)(w[e] & 0xffffu);
-      t[ch * 8 + 2 * e + 1][pos] = (uint16_t)(w[e] >> 16);
-    }
-  }
-  if (vmax_blk) {  // the block's max |V|: waves, then the four wave results
-    __shared__ float red[4];
-    for (int off = 32; off > 0; off >>= 1) {
-      const float o = __shfl_xor(vmax, off);
-      vmax = (o > vmax || o != o) ? o : vmax;
-    }
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = vmax;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float m = red[0];
-      for (int i = 1; i < 4; ++i) m = (red[i] > m || red[i] != red[i]) ? red[i] : m;
-      vmax_blk[(size_t)bh * gridDim.x + blockIdx.x] = m;
-    }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < D * (TK / 8); i += 256) {
-    const int c = i / (TK / 8), q = i % (TK / 8);
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)t[c][q * 8 + 2 * e] | ((uint32_t)t[c][q * 8 + 2 * e + 1] << 16);
-    *reinterpret_cast<uint4*>(dst + (size_t)c * Nk_pad + kt + q * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
 // Compute units of the current device (cached per device; 0 if unknown).
 int cu_count() {
   static std::atomic<int> cache[64];
@@ -747,16 +684,6 @@ hipError_t launch_d(const AttnArgs& a, bool fixed, const uint16_t* vt, int nk_pa
 }
 
 }  // namespace
-
-hipError_t launch_transpose_v(const void* v, void* vt, int BH, int Nk, int d, hipStream_t s, float* vmax_blk) {
-  const dim3 grid((unsigned)(vt_pad(Nk) / 64), (unsigned)BH);
-  const uint16_t* src = static_cast<const uint16_t*>(v);
-  uint16_t* dst = static_cast<uint16_t*>(vt);
-  if (d == 128) transpose_v<128><<<grid, 256, 0, s>>>(src, dst, Nk, vt_pad(Nk), vmax_blk);
-  else if (d == 64) transpose_v<64><<<grid, 256, 0, s>>>(src, dst, Nk, vt_pad(Nk), vmax_blk);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
 
 hipError_t launch_attn_bf16(const AttnArgs& a, bool fixed, const void* vt, hipStream_t s) {
   const int nk_pad = vt_pad(a.Nk);

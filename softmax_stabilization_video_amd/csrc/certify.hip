@@ -93,7 +93,7 @@ cert_keys_values(const T* __restrict__ K, const T* __restrict__ V, int Nk, int S
   constexpr int VEC = Vec<T>::n, TPR = D / VEC, RPI = kThreads / TPR;
   __shared__ double colsum[RPI][D];
   __shared__ double red[kThreads / 64];
-  const int bh = blockIdx.y, split = blockIdx.x;
+  const int bh = blockIdx.x / Sk, split = blockIdx.x % Sk;  // 1-D grid: any head count
   int lo, hi;
   split_range(Nk, Sk, split, &lo, &hi);
   const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
@@ -183,14 +183,14 @@ cert_norms(const T* __restrict__ Q, const T* __restrict__ K, const double* __res
            double* __restrict__ kap_part, double* __restrict__ qss_part) {
   constexpr int VEC = Vec<T>::n, TPR = D / VEC, RPI = kThreads / TPR;
   __shared__ double red[kThreads / 64];
-  const int bh = blockIdx.y;
+  const int bh = blockIdx.x / (Sk + Sq), part = blockIdx.x % (Sk + Sq);  // 1-D grid: any head count
   const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
   double kb[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) kb[e] = kbar[(size_t)bh * D + tc * VEC + e];
   double best = 0.0;
-  if ((int)blockIdx.x < Sk) {
-    const int split = blockIdx.x;
+  if (part < Sk) {
+    const int split = part;
     int lo, hi;
     split_range(Nk, Sk, split, &lo, &hi);
     const T* base = K + (size_t)bh * Nk * D;
@@ -223,7 +223,7 @@ cert_norms(const T* __restrict__ Q, const T* __restrict__ K, const double* __res
     best = block_max(best, red);
     if (threadIdx.x == 0) kap_part[(size_t)bh * Sk + split] = best;
   } else {
-    const int split = blockIdx.x - Sk;
+    const int split = part - Sk;
     int lo, hi;
     split_range(Nq, Sq, split, &lo, &hi);
     const T* base = Q + (size_t)bh * Nq * D;
@@ -345,11 +345,12 @@ hipError_t certify_typed(const CertifyArgs& a, hipStream_t s) {
   const T* q = static_cast<const T*>(a.q);
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
-  cert_keys_values<T, D><<<dim3(Sk, BH), kThreads, 0, s>>>(k, a.vmax_blk ? nullptr : v, a.Nk, Sk, a.ksum_part,
-                                                             a.vmax_part);
+  if ((long long)BH * (Sk + Sq) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  cert_keys_values<T, D><<<(unsigned)(BH * Sk), kThreads, 0, s>>>(k, a.vmax_blk ? nullptr : v, a.Nk, Sk,
+                                                                   a.ksum_part, a.vmax_part);
   cert_kbar<D><<<BH, D, 0, s>>>(a.ksum_part, a.Nk, Sk, a.kbar, a.vmax_blk, a.vmax_nblk, a.vmax_part);
-  cert_norms<T, D><<<dim3(Sk + Sq, BH), kThreads, 0, s>>>(q, k, a.kbar, a.Nq, a.Nk, Sk, Sq, c2, a.mu,
-                                                          a.kap_part, a.qss_part);
+  cert_norms<T, D><<<(unsigned)(BH * (Sk + Sq)), kThreads, 0, s>>>(q, k, a.kbar, a.Nq, a.Nk, Sk, Sq, c2, a.mu,
+                                                                    a.kap_part, a.qss_part);
   const int fb = (BH + kThreads - 1) / kThreads;
   cert_finalize<<<fb, kThreads, 0, s>>>(a.vmax_part, a.kap_part, a.qss_part, BH, a.Nk, Sk, Sq, c2,
                                         a.cert, a.stats);
