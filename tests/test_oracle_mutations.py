@@ -47,6 +47,16 @@ MUTANTS = {
     "partial_ignores_start": ("for (int64_t j = k0; j < end; ++j) {", "for (int64_t j = 0; j < end; ++j) {"),
     "partial_ignores_causal": ("const int64_t end = k1 < n ? k1 : n;", "const int64_t end = k1 < nk ? k1 : nk;"),
     "partial_mu_sign": ("const double p = exp2(c2 * dot - mu[i]);", "const double p = exp2(c2 * dot + mu[i]);"),
+    "kappa_drops_sqrt": ("kappa = max_keep_nan(kappa, sqrt(ss));", "kappa = max_keep_nan(kappa, ss);"),
+    "qnorm_drops_sqrt": ("const double qn = sqrt(ss);", "const double qn = ss;"),
+    "qmax_first_row_only": ("double qmax = 0.0, bound = 0.0;\n  for (int64_t r = 0; r < nq; ++r) {",
+                            "double qmax = 0.0, bound = 0.0;\n  for (int64_t r = 0; r < 1; ++r) {"),
+    "keys_exponent_is_floor": ("const int32_t L = ceil_log2_exact((double)nk);",
+                               "const int32_t L = (int32_t)floor(log2((double)nk));"),
+    "G_without_floor_of_one": ("ceil_log2_exact(vmax > 1.0 ? vmax : 1.0)", "ceil_log2_exact(vmax)"),
+    "fixed_mu_uses_row0_mu": ("const double x = c2 * s[j] - mu[i];", "const double x = c2 * s[j] - mu[0];"),
+    "fixed_mu_drops_log2e": ("const double x = c2 * s[j] - mu[i];", "const double x = scale * s[j] - mu[i];"),
+    "max_drops_nan_argument": ("if (isnan(acc) || isnan(x)) return NAN;", "if (isnan(acc)) return NAN;"),
 }
 
 
