@@ -354,6 +354,10 @@ def main(argv=None):
         "step_ms_min_events": round(min(step_events), 4),
         "step_ms_mean_events": round(statistics.mean(step_events), 4),
     }
+    props = torch.cuda.get_device_properties(q.device)
+    out["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                     "compute_units": props.multi_processor_count,
+                     "memory_gib": round(props.total_memory / 2 ** 30, 1)}
     if "clis_kernel_ms" in res:
         out["clis_kernel_tflops"] = round(flops / res["clis_kernel_ms"] / 1e9, 2)
         out["clis_kernel_ms"] = round(res["clis_kernel_ms"], 4)
