@@ -55,6 +55,7 @@ LSE_CASES = [
     ("bf16_tail_d128", 1, 2, 1000, 1000, 128, "bf16", False),
     ("bf16_causal_tail", 1, 3, 777, 777, 128, "bf16", True),
     ("bf16_cross_d64", 2, 1, 300, 1300, 64, "bf16", False),
+    ("bf16_causal_d64", 2, 1, 300, 300, 64, "bf16", True),
     ("bf16_one_key", 1, 2, 70, 1, 128, "bf16", False),
     ("fp32_tail_d64", 1, 2, 1000, 1000, 64, "fp32", False),
     ("fp32_causal", 1, 2, 700, 700, 128, "fp32", True),
@@ -133,6 +134,7 @@ SHARD_CASES = [
     ("bf16_dense", 1, 2, 700, 1000, 128, "bf16", False, [0, 384, 700, 1000]),
     ("bf16_causal", 1, 2, 777, 777, 128, "bf16", True, [0, 256, 300, 777]),
     ("bf16_d64_one_key_shard", 2, 1, 200, 450, 64, "bf16", False, [0, 1, 449, 450]),
+    ("bf16_causal_d64", 1, 3, 520, 520, 64, "bf16", True, [0, 64, 200, 520]),
     ("fp32_dense", 1, 2, 300, 500, 64, "fp32", False, [0, 128, 500]),
     ("fp32_causal", 1, 1, 333, 333, 128, "fp32", True, [0, 100, 333]),
 ]
