@@ -42,7 +42,7 @@ def dominant_kernel(w):
     """(name, source) of the fixed-stabilizer kernel that runs this workload."""
     c = "true" if w.causal else "false"
     if w.dtype == "bf16":
-        return f"attn_fwd_bf16<{w.d}, true, {c}, 8, false, false, true>", os.path.join(CSRC, "attn_bf16.hip")
+        return f"attn_fwd_bf16<{w.d}, true, {c}, 8, false, false>", os.path.join(CSRC, "attn_bf16.hip")
     return f"attn_fwd_fp32<{w.d}, true, {c}, false>", os.path.join(CSRC, "attn_fp32.hip")
 
 

@@ -202,6 +202,7 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
     f.tail_o = at<float>(ws, L.tail_o);
     f.tail_l = at<float>(ws, L.tail_l);
     f.sched = counts + 2;  // zeroed by the route kernel above
+    f.split_heads = counts + 4;
     f.mu = mu_use;
     f.head_list = lists;
     f.head_count = counts;

@@ -13,11 +13,12 @@
 //             stabilizer in use moves, and the accumulators are rescaled, only
 //             when a row's tile maximum exceeds it by more than kLazyTau (log2
 //             units), under a wave-uniform branch; weights stay <= 2^kLazyTau.
-// The fixed form has three more switches: PARTIAL (key shards: fp32
-// unnormalized sums in and out), PRESCALE (when only O is wanted, the query
-// fragments are pre-multiplied by c and the score products start from -mu, so
-// a weight is one exp2 of the accumulator), and, for the dense non-shard
-// form, the last-round key splits below.  The fixed and online forms use
+// The fixed form has two more switches: PARTIAL (key shards: fp32
+// unnormalized sums in and out) and, for the dense non-shard form, the
+// last-round key splits below.  Every fixed form evaluates the exp2 argument
+// as x = fma(s, c, -mu) in fp32 from the fp32 score s = q.k and the exact bf16
+// inputs, so x stays within fp32 rounding of c q.k - mu: the quantity the
+// certificate bounds.  The fixed and online forms use
 // independently tuned workgroup sizes (the pages tune tiles per method too,
 // Table 7 caption).
 //
@@ -47,10 +48,7 @@
 //
 // Outputs.  Normally O = O_acc / l in bf16, and optionally each row's
 // log-sum-exp ln 2 * (m + log2 l), where m is the fixed mu_i or the final
-// running maximum (both in log2 units).  The log-sum-exp comes from the fixed
-// form without PRESCALE: rounding c q to bf16 (error e) shifts every score of
-// a row by the common term e.kbar plus a small key-dependent part, and the
-// common term cancels in O but not in ln l.  With o_acc set (fixed variant
+// running maximum (both in log2 units).  With o_acc set (fixed variant
 // only, for key-value shards) the kernel instead starts from, or overwrites,
 // fp32 unnormalized sums o_acc and l_acc: with a fixed stabilizer the sums
 // over disjoint key ranges simply add.  kv_offset is the global index of key 0
@@ -111,7 +109,7 @@ constexpr int kXcds = 8;                  // MI355X: workgroups are dealt round-
 constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor word 3 (untyped 32-bit data)
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLazyTau = 8.f;  // log2 units: lazy-rescale weights stay <= 256
-constexpr int kMaxSplit = 8;     // key splits per pool item
+constexpr int kMaxSplit = kTailSplits;  // key splits per split item
 #ifndef CLIS_POOL_DIV
 #define CLIS_POOL_DIV 10         // pool: at least 1 / CLIS_POOL_DIV of the items (0: the last round only)
 #endif
@@ -119,28 +117,44 @@ constexpr int kMaxSplit = 8;     // key splits per pool item
 #define CLIS_POOL_OVER 50        // pool workgroups launched beyond one per claim, in percent
 #endif
 
-// Work of the dense fixed form: `active` items (query tiles of the routed
-// heads).  The first F run one workgroup each, in XCD-local order.  The last
-// P form a pool: its first P1 items whole, then P2 items as kMaxSplit key
-// splits each (fp32 partial sums in the tail buffers, added in split order by
-// tail_combine).  The workgroups after the first F each claim one pool entry
-// (a whole item or a split) from a device counter when they start, and exit
-// if none is left (or at once when the pool is empty, e.g. when no head is
-// routed to the kernel).  There are more of them than entries, and an XCD reaches
-// its share of them once its own items are under way, so XCDs that run faster
-// (the XCDs of one GPU run at different clocks under load) claim more of the
-// pool; the splits at its end even out the last round.
+// Work of the dense forms: `active` items (query tiles of the routed heads).
+// In the fixed form the last query tile of each of the first S listed heads
+// whose index is below kSplitHeads (S is counted by the route kernel) is cut
+// into kTailSplits key splits (fp32 partial sums in the tail buffers, added
+// in split order by tail_combine); which items are cut is a function of the
+// head alone, so a head's output bits do not depend on the other heads routed
+// with it.  Of the W = active - S whole items, the first F run one workgroup
+// each, in XCD-local order; the last P1 whole items and then the S * 8 splits
+// form a pool.  The workgroups after the first F each claim one pool entry
+// from a device counter when they start, and exit if none is left (or at once
+// when the pool is empty, e.g. when no head is routed to the kernel).  There
+// are more of them than entries, and an XCD reaches its share of them once
+// its own items are under way, so XCDs that run faster (the XCDs of one GPU
+// run at different clocks under load) claim more of the pool; the splits at
+// its end even out the last round.
 struct PoolPlan {
-  int F, P1, P2;
+  int F, P1, S;
 };
-__host__ __device__ inline PoolPlan pool_plan(int active, int conc, bool splits) {
-  PoolPlan t{active, 0, 0};
-  if (conc <= 0 || active <= 0) return t;
-  int P = max(active % conc, CLIS_POOL_DIV > 0 ? active / CLIS_POOL_DIV : 0);
-  P = min(P, active);
-  const int P2 = splits ? min(P, kTailSlots / kMaxSplit) : 0;
-  t = PoolPlan{active - P, P - P2, P2};
-  return t;
+__host__ __device__ inline PoolPlan pool_plan(int active, int conc, int S) {
+  if (conc <= 0 || active <= 0) return PoolPlan{active, 0, 0};
+  const int W = active - S;
+  const int P = max(active % conc, CLIS_POOL_DIV > 0 ? active / CLIS_POOL_DIV : 0);
+  const int P1 = min(W, max(0, P - S));
+  return PoolPlan{W - P1, P1, S};
+}
+
+// Whole item w (0 <= w < active - S) -> (slot in the head list, query tile):
+// the first S heads contribute their first n_qt - 1 tiles, the others all.
+__device__ __forceinline__ void whole_item(int w, int S, int n_qt, int* slot, int* qt) {
+  const int a = S * (n_qt - 1);
+  if (w < a) {
+    *slot = w / (n_qt - 1);
+    *qt = w % (n_qt - 1);
+  } else {
+    const int x = w - a;
+    *slot = S + x / n_qt;
+    *qt = x % n_qt;
+  }
 }
 
 __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, const floatx16& c) {
@@ -199,7 +213,7 @@ __device__ __forceinline__ void load_tiles(const char* Kh, const char* Vth, int 
   }
 }
 
-template <int D, bool FIXED, bool CAUSAL, int WAVES, bool PARTIAL, bool LAZY, bool PRESCALE>
+template <int D, bool FIXED, bool CAUSAL, int WAVES, bool PARTIAL, bool LAZY>
 __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2)
 attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ Vt, uint16_t* __restrict__ O,
@@ -207,27 +221,30 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const int32_t* __restrict__ head_count, int n_slots, int Nq, int Nk, int Nk_pad, float c2,
               float* __restrict__ lse, float* __restrict__ o_acc, float* __restrict__ l_acc, int accumulate,
               int kv_offset_arg, float* __restrict__ tail_o, float* __restrict__ tail_l, int pool_conc,
-              int* __restrict__ sched) {
+              int* __restrict__ sched, const int32_t* __restrict__ split_heads) {
   static_assert(FIXED || !PARTIAL, "key shards use the fixed stabilizer");
   static_assert(!(FIXED && LAZY), "lazy rescaling is an online-softmax form");
-  static_assert(!PRESCALE || (FIXED && !PARTIAL), "pre-scaled queries: fixed path, output O only");
   using G = Geo<D, WAVES>;
   const int kv_offset = PARTIAL ? kv_offset_arg : 0;  // global index of key 0
   constexpr int NS = G::NS, NC = G::NC, BM = G::BM;
   __shared__ __attribute__((aligned(1024))) char lds[2 * G::STAGE_BYTES];  // [stage][K tile, V^T tile]
 
-  constexpr bool TAIL = FIXED && !PARTIAL && !CAUSAL;  // last-round key splits
+  constexpr bool TAIL = FIXED && !PARTIAL && !CAUSAL;  // key splits of the pool
   const int n_qt = (Nq + BM - 1) / BM;
-  const int active = (head_list ? *head_count : n_slots) * n_qt;
-  int lid, split = -1, nsplit = 1;  // split: this workgroup's slot in the tail buffers
+  const int n_heads = head_list ? *head_count : n_slots;
+  const int active = n_heads * n_qt;
+  int split = -1, nsplit = 1;  // split: this workgroup's slot in the tail buffers
   static_assert(!TAIL || BM <= kTailRows, "tail buffers hold kTailRows rows per workgroup");
+  int slot, qt;
   if (!PARTIAL && !CAUSAL && sched) {  // pooled work (file comment)
-    const PoolPlan pp = pool_plan(active, pool_conc, TAIL && tail_o);
+    const int S = (TAIL && tail_o) ? (split_heads ? *split_heads : head_list ? 0 : min(n_slots, kSplitHeads)) : 0;
+    const PoolPlan pp = pool_plan(active, pool_conc, S);
     const int b = blockIdx.x;
+    int w;  // whole item, or -1 for a key split
     if (b < pp.F) {
-      lid = xcd_remap(b, pp.F);
+      w = xcd_remap(b, pp.F);
     } else {  // pool workgroup: claim one entry
-      const int entries = pp.P1 + pp.P2 * kMaxSplit;
+      const int entries = pp.P1 + pp.S * kMaxSplit;
       if (entries == 0) return;  // nothing pooled (no head routed to this kernel)
       // broadcast through LDS stage 1, which the second tile's load first
       // writes after a barrier every wave reaches past this read (a separate
@@ -243,37 +260,42 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       __syncthreads();
       const int c = *claim;
       if (c < pp.P1) {  // a whole item
-        lid = pp.F + c;
+        w = pp.F + c;
       } else {
         split = c - pp.P1;  // a key split: its slot in the tail buffers
-        if (!TAIL || split >= pp.P2 * kMaxSplit) return;
+        if (!TAIL || split >= pp.S * kMaxSplit) return;
         nsplit = kMaxSplit;
-        lid = pp.F + pp.P1 + split / kMaxSplit;
+        w = -1;
       }
+    }
+    if (w >= 0) {
+      whole_item(w, pp.S, n_qt, &slot, &qt);
+    } else {
+      slot = split / kMaxSplit;
+      qt = n_qt - 1;
     }
   } else {
     if ((int)blockIdx.x >= active) return;
-    lid = xcd_remap(blockIdx.x, active);
-  }
-  int slot, qt;
-  if constexpr (CAUSAL) {
-    // Longest query tiles first, with heads taken in groups of G.  An XCD
-    // deals consecutive workgroups round-robin to its four shader engines and
-    // waits, in order, for a free CU in the next one, so every four
-    // consecutive workgroups should be of (nearly) equal length and each
-    // engine's total work equal: the G heads of a group advance together,
-    // through their query tiles in blocks of M = 4 / G, every other block in
-    // reverse.
-    constexpr int G = CLIS_CAUSAL_GROUP, M = 4 / G;
-    static_assert(G == 1 || G == 2 || G == 4, "heads per group: 1, 2 or 4");
-    const int heads = active / n_qt, grp = lid / (G * n_qt);
-    const int width = min(G, heads - G * grp), r = lid - G * n_qt * grp;
-    slot = G * grp + r % width;
-    const int p = r / width, blk = p / M, e = p % M, top = n_qt - 1 - M * blk;
-    qt = (blk % 2 == 1 && blk < n_qt / M) ? top - (M - 1) + e : top - e;
-  } else {
-    slot = lid / n_qt;
-    qt = lid % n_qt;
+    const int lid = xcd_remap(blockIdx.x, active);
+    if constexpr (CAUSAL) {
+      // Longest query tiles first, with heads taken in groups of G.  An XCD
+      // deals consecutive workgroups round-robin to its four shader engines and
+      // waits, in order, for a free CU in the next one, so every four
+      // consecutive workgroups should be of (nearly) equal length and each
+      // engine's total work equal: the G heads of a group advance together,
+      // through their query tiles in blocks of M = 4 / G, every other block in
+      // reverse.
+      constexpr int G = CLIS_CAUSAL_GROUP, M = 4 / G;
+      static_assert(G == 1 || G == 2 || G == 4, "heads per group: 1, 2 or 4");
+      const int heads = active / n_qt, grp = lid / (G * n_qt);
+      const int width = min(G, heads - G * grp), r = lid - G * n_qt * grp;
+      slot = G * grp + r % width;
+      const int p = r / width, blk = p / M, e = p % M, top = n_qt - 1 - M * blk;
+      qt = (blk % 2 == 1 && blk < n_qt / M) ? top - (M - 1) + e : top - e;
+    } else {
+      slot = lid / n_qt;
+      qt = lid % n_qt;
+    }
   }
   const int bh = head_list ? head_list[slot] : slot;
 
@@ -333,18 +355,6 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
   float mrow = FIXED ? (qvalid ? mu[(size_t)bh * Nq + qrow] : 0.f) : -INFINITY;
   const float negmu = -mrow;
-  // PRESCALE: the query fragments hold q' = bf16(c q) and every score product
-  // starts from -mu, so each accumulator ends as the exp2 argument
-  // x = c q.k - mu itself and a weight costs one v_exp_f32 (no fma per score).
-  floatx16 nmu;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) nmu[r] = negmu;
-  if constexpr (PRESCALE) {
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)((float)qf[s][e] * c2);  // round to nearest even
-  }
   float lsum = 0.f;
   floatx16 oacc[NC];
 #pragma unroll
@@ -373,7 +383,6 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     floatx16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    if constexpr (PRESCALE) acc = nmu;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       acc = mfma32(*reinterpret_cast<const bf16x8*>(Ks + kb * 32 * D * 2 + kro[s]), qf[s], acc);
@@ -410,14 +419,13 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const char* Ks = lds + ST * G::STAGE_BYTES;
     const char* Vs = Ks + G::TILE_BYTES;
     if constexpr (FIXED) {
-      // no running maximum: x = c s - mu with mu fixed, weights 2^x (with
-      // PRESCALE the accumulators already hold x)
+      // no running maximum: x = c s - mu with mu fixed, weights 2^x
       (void)need_mask;
       auto weights = [&](const floatx16& sacc, int kb, uint32_t* pw) {
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(PRESCALE ? sacc[r] : fmaf(sacc[r], c2, negmu));
+          p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], c2, negmu));
           if constexpr (MASK) p[r] = visible(kt, kb, r) ? p[r] : 0.f;
         }
         pack(p, pw);
@@ -554,8 +562,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     return;
   }
   const float inv = 1.f / lsum;
-  if constexpr (!PRESCALE)
-    if (qvalid && lse && g == 0) lse[(size_t)bh * Nq + qrow] = kLn2 * ((FIXED ? -negmu : mrow) + log2f(lsum));
+  if (qvalid && lse && g == 0) lse[(size_t)bh * Nq + qrow] = kLn2 * ((FIXED ? -negmu : mrow) + log2f(lsum));
   if (qvalid) {
     uint16_t* orow = O + qoff;
 #pragma unroll
@@ -571,22 +578,20 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 }
 
 // Finishes the pool's key splits: workgroup t sums the kMaxSplit parts of the
-// t-th split item in split order, then O = sum o / sum l (and the log-sum-exp
-// when asked), for the rows that exist.  256 threads: each handles 4 channels
-// of one row per pass.
+// t-th split item (the last query tile of list slot t) in split order, then
+// O = sum o / sum l (and the log-sum-exp when asked), for the rows that
+// exist.  256 threads: each handles 4 channels of one row per pass.
 template <int D, int BM>
 __global__ void __launch_bounds__(256)
 tail_combine(const float* __restrict__ tail_o, const float* __restrict__ tail_l, uint16_t* __restrict__ O,
              const float* __restrict__ mu, float* __restrict__ lse, const int32_t* __restrict__ head_list,
-             const int32_t* __restrict__ head_count, int n_slots, int Nq, int pool_conc) {
+             const int32_t* __restrict__ split_heads, int n_slots, int Nq) {
   constexpr int GROUPS = D / 4, ROWS = 256 / GROUPS;  // rows per pass
   const int n_qt = (Nq + BM - 1) / BM;
-  const int active = (head_list ? *head_count : n_slots) * n_qt;
-  const PoolPlan pp = pool_plan(active, pool_conc, true);
+  const int S = split_heads ? *split_heads : head_list ? 0 : min(n_slots, kSplitHeads);
   const int t = blockIdx.x;
-  if (t >= pp.P2) return;
-  const int lid = pp.F + pp.P1 + t;
-  const int slot = lid / n_qt, qt = lid % n_qt;
+  if (t >= S) return;
+  const int slot = t, qt = n_qt - 1;
   const int bh = head_list ? head_list[slot] : slot;
   const int cg = threadIdx.x % GROUPS, r0 = threadIdx.x / GROUPS;
   for (int r = r0; r < BM; r += ROWS) {
@@ -623,7 +628,7 @@ int cu_count() {
   return n;
 }
 
-template <int D, bool FIXED, bool CAUSAL, bool PARTIAL = false, bool LAZY = false, bool PRESCALE = false>
+template <int D, bool FIXED, bool CAUSAL, bool PARTIAL = false, bool LAZY = false>
 hipError_t launch_t(const AttnArgs& a, const uint16_t* vt, int nk_pad, hipStream_t s) {
   constexpr int WAVES = FIXED ? (CAUSAL ? CLIS_FIXED_CAUSAL_WAVES : CLIS_FIXED_WAVES) : CLIS_ONLINE_WAVES;
   using G = Geo<D, WAVES>;
@@ -638,30 +643,30 @@ hipError_t launch_t(const AttnArgs& a, const uint16_t* vt, int nk_pad, hipStream
   long long blocks = (long long)n_qt * a.n_slots;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (conc > 0) {
-    // Pool workgroups.  The device routes active <= blocks items; the
-    // blocks - F >= P1 + P2 workgroups past its F claim too, and it has
-    // P1 + P2 * kMaxSplit entries, so (kMaxSplit - 1) * P2 extra workgroups
-    // suffice for any active, with P <= pmax = min(blocks, max(conc - 1,
-    // blocks / CLIS_POOL_DIV)) and P2 <= min(pmax, kTailSlots / kMaxSplit).
-    // CLIS_POOL_OVER percent more of every entry's worth lets faster XCDs
-    // claim more.
+    // Pool workgroups.  With active <= blocks items of which S are split, the
+    // first F = active - S - P1 workgroups run whole items and the rest claim
+    // from P1 + S * kMaxSplit entries, so blocks + (kMaxSplit - 1) * Smax
+    // workgroups cover every entry for any active and S <= Smax =
+    // min(n_slots, kSplitHeads), with P1 <= pmax = min(blocks, max(conc - 1,
+    // blocks / CLIS_POOL_DIV)).  CLIS_POOL_OVER percent more of every entry's
+    // worth lets faster XCDs claim more.
     const long long div = CLIS_POOL_DIV > 0 ? blocks / CLIS_POOL_DIV : 0;
     const long long pmax = std::min<long long>(blocks, std::max<long long>(conc - 1, div));
-    const long long p2max = splits ? std::min<long long>(pmax, kTailSlots / kMaxSplit) : 0;
-    blocks += (kMaxSplit - 1) * p2max + (pmax + (kMaxSplit - 1) * p2max) * CLIS_POOL_OVER / 100;
+    const long long smax = splits ? std::min<long long>(a.n_slots, kSplitHeads) : 0;
+    blocks += (kMaxSplit - 1) * smax + (pmax + kMaxSplit * smax) * CLIS_POOL_OVER / 100;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   }
-  attn_fwd_bf16<D, FIXED, CAUSAL, WAVES, PARTIAL, LAZY, PRESCALE><<<(unsigned)blocks, G::THREADS, 0, s>>>(
+  attn_fwd_bf16<D, FIXED, CAUSAL, WAVES, PARTIAL, LAZY><<<(unsigned)blocks, G::THREADS, 0, s>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), vt, static_cast<uint16_t*>(a.o),
       a.mu, a.head_list, a.head_count, a.n_slots, a.Nq, a.Nk, nk_pad, a.c2, a.lse, a.o_acc, a.l_acc,
-      a.accumulate, a.kv_offset, a.tail_o, a.tail_l, conc, conc > 0 ? a.sched : nullptr);
+      a.accumulate, a.kv_offset, a.tail_o, a.tail_l, conc, conc > 0 ? a.sched : nullptr, a.split_heads);
   if constexpr (TAIL) {
     if (conc > 0 && splits) {  // one workgroup per possible split item
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      tail_combine<D, G::BM><<<(unsigned)(kTailSlots / kMaxSplit), 256, 0, s>>>(
-          a.tail_o, a.tail_l, static_cast<uint16_t*>(a.o), a.mu, a.lse, a.head_list, a.head_count, a.n_slots,
-          a.Nq, conc);
+      tail_combine<D, G::BM><<<(unsigned)kSplitHeads, 256, 0, s>>>(
+          a.tail_o, a.tail_l, static_cast<uint16_t*>(a.o), a.mu, a.lse, a.head_list, a.split_heads, a.n_slots,
+          a.Nq);
     }
   }
   return hipGetLastError();
@@ -673,9 +678,6 @@ hipError_t launch_d(const AttnArgs& a, bool fixed, const uint16_t* vt, int nk_pa
     if (!fixed) return hipErrorInvalidValue;
     return a.causal ? launch_t<D, true, true, true>(a, vt, nk_pad, s) : launch_t<D, true, false, true>(a, vt, nk_pad, s);
   }
-  if (fixed && !a.lse)  // output O only: pre-scaled queries
-    return a.causal ? launch_t<D, true, true, false, false, true>(a, vt, nk_pad, s)
-                    : launch_t<D, true, false, false, false, true>(a, vt, nk_pad, s);
   if (fixed) return a.causal ? launch_t<D, true, true>(a, vt, nk_pad, s) : launch_t<D, true, false>(a, vt, nk_pad, s);
   if (a.lazy)
     return a.causal ? launch_t<D, false, true, false, true>(a, vt, nk_pad, s)

@@ -313,7 +313,7 @@ route_heads(const int32_t* __restrict__ cert, int mode, int BH, int32_t* __restr
             int32_t* __restrict__ counts, int32_t* __restrict__ route_out) {
   // One wave compacts the heads in index order: ballot + prefix popcount.
   const int lane = threadIdx.x;
-  int nf = 0, no = 0;
+  int nf = 0, no = 0, nsplit = 0;
   for (int base = 0; base < BH; base += 64) {
     const int h = base + lane;
     int fixed = 0;
@@ -326,6 +326,7 @@ route_heads(const int32_t* __restrict__ cert, int mode, int BH, int32_t* __restr
       else lists[BH + no + __popcll(om & below)] = h;
       if (route_out) route_out[h] = fixed;
     }
+    if (base == 0) nsplit = __popcll(fm & ((1ull << kSplitHeads) - 1));  // heads 0 .. kSplitHeads-1
     nf += __popcll(fm);
     no += __popcll(om);
   }
@@ -334,6 +335,7 @@ route_heads(const int32_t* __restrict__ cert, int mode, int BH, int32_t* __restr
     counts[1] = no;
     counts[2] = 0;  // work counters of the attention kernels that follow
     counts[3] = 0;
+    counts[4] = nsplit;
   }
 }
 

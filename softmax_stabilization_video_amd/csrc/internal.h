@@ -35,7 +35,7 @@ struct WsLayout {
   size_t mu;         // [BH][Nq]    fp32   stabilizers when the caller gave none
   size_t cert;       // [BH]        int32
   size_t lists;      // [2][BH]     int32  heads routed fixed / online
-  size_t counts;     // [4]         int32  list lengths, then work counters
+  size_t counts;     // [8]         int32  list lengths, work counters, split heads
   size_t vt;         // [BH][d][Nk_pad] bf16  V^T for the bf16 attention kernels
   size_t vmax_blk;   // [BH][vt_pad(Nk) / 64] fp32  max |V| per 64-key block, from the V transpose
   size_t tail_o;     // [kTailSlots][kTailRows][d] fp32  key-split partial sums of the pool
@@ -45,10 +45,15 @@ struct WsLayout {
 
 // Key splits at the end of the fixed kernel's pool of work items: at most
 // kTailSlots splits of kTailRows query rows each; kPoolWorkers caps the
-// workgroups resident at once that the pool is sized for.
+// workgroups resident at once that the pool is sized for.  The items cut into
+// kTailSplits key splits are the last query tiles of the heads with index
+// below kSplitHeads that the kernel runs: a function of the head alone, so a
+// head's result does not depend on which other heads are routed with it.
 constexpr int kTailSlots = 256;
 constexpr int kTailRows = 256;
 constexpr int kPoolWorkers = 256;
+constexpr int kTailSplits = 8;
+constexpr int kSplitHeads = kTailSlots / kTailSplits;
 
 // Keys of the V^T copy, padded to whole 128-key tiles (either tile size).
 inline int vt_pad(int Nk) { return (Nk + 127) / 128 * 128; }
@@ -66,7 +71,7 @@ inline WsLayout ws_layout(int B, int H, int Nq, int Nk, int d) {
   w.mu = o;        o = align256(o + BH * (size_t)Nq * sizeof(float));
   w.cert = o;      o = align256(o + BH * sizeof(int32_t));
   w.lists = o;     o = align256(o + 2 * BH * sizeof(int32_t));
-  w.counts = o;    o = align256(o + 4 * sizeof(int32_t));
+  w.counts = o;    o = align256(o + 8 * sizeof(int32_t));
   w.vt = o;        o = align256(o + BH * (size_t)d * vt_pad(Nk) * 2);
   w.vmax_blk = o;  o = align256(o + BH * (size_t)(vt_pad(Nk) / 64) * sizeof(float));
   w.tail_o = o;    o = align256(o + (size_t)kTailSlots * kTailRows * d * sizeof(float));
@@ -94,7 +99,8 @@ struct CertifyArgs {
 hipError_t launch_certify(const CertifyArgs& a, hipStream_t s);
 
 // Builds the fixed / online head lists from cert and mode (one tiny kernel);
-// counts[0..1] receive the list lengths, counts[2..3] (work counters) zero.
+// counts[0..1] receive the list lengths, counts[2..3] (work counters) zero,
+// counts[4] the number of fixed-routed heads with index < kSplitHeads.
 hipError_t launch_route(const int32_t* cert, int mode, int BH, int32_t* lists, int32_t* counts,
                         int32_t* route_out, hipStream_t s);
 
@@ -118,6 +124,7 @@ struct AttnArgs {
   float* tail_o = nullptr;    // [kTailSlots][kTailRows][d], or NULL: no splits
   float* tail_l = nullptr;    // [kTailSlots][kTailRows]
   int* sched = nullptr;       // pool counter, zero at launch, or NULL: no pool
+  const int32_t* split_heads = nullptr;  // device count of listed heads < kSplitHeads
 };
 
 // bf16 kernels: V is read through a transposed copy [BH][d][vt_pad(Nk)]

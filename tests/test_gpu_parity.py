@@ -9,8 +9,9 @@ summation orders could disagree.
 Attention: bf16 within max abs 2e-2, mean abs 1e-3 and rel L2 5e-3 of the
 oracle; fp32 within max abs 1e-5; in every mode (fixed, online, online with
 lazy rescaling, auto).  Routing: auto mode's output for every head equals the
-forced mode of the route it took, bitwise except where the dense fixed
-kernel's last-round key splits cover other rows (then within one bf16 ulp).
+forced mode of the route it took, bitwise (which query tiles the dense fixed
+kernel cuts into key splits depends on the head alone, not on which other
+heads are routed with it).
 """
 import math
 
@@ -62,19 +63,10 @@ def check_certify(clis, w, host, dev, margin=1e-9):
     return mu, cert, ref
 
 
-def assert_same_kernel(a, b, exact: bool, what: str = ""):
-    """Outputs of the same kernel on the same head.  The dense fixed kernel
-    splits the keys of its last round of workgroups, and which query tiles
-    fall in that round depends on how many heads it runs: with a different
-    head count (auto mode with mixed routes against forced fixed mode) a row
-    may add its key splits in another order, which changes fp32 rounding
-    only.  Bitwise otherwise."""
+def assert_same_kernel(a, b, what: str = ""):
+    """Outputs of the same kernel on the same head: bitwise equal."""
     import torch
-    if exact:
-        assert torch.equal(a, b), what
-        return
-    x, y = a.float(), b.float()
-    assert bool(((x - y).abs() <= 2.0 ** -7 * y.abs() + 1e-6).all()), what  # one bf16 ulp
+    assert torch.equal(a, b), what
 
 
 def run_attention(clis, w, host, dev, mu, cert, rows=None, modes=("fixed", "online", "online_lazy", "auto")):
@@ -107,8 +99,7 @@ def run_attention(clis, w, host, dev, mu, cert, rows=None, modes=("fixed", "onli
         for b in range(w.B):
             for h in range(w.H):
                 ref = outs["fixed"] if c[b, h] else outs["online"]
-                assert_same_kernel(outs["auto"][b, h], ref[b, h], exact=bool(c.all() or not c[b, h]),
-                                   what=f"{w.name} auto head {(b, h)}")
+                assert_same_kernel(outs["auto"][b, h], ref[b, h], what=f"{w.name} auto head {(b, h)}")
     return outs, errs
 
 
@@ -154,13 +145,14 @@ def test_small_shapes_all_rows(clis, case):
 
 
 def test_mixed_routing_small(clis):
-    """A quarter of the heads scaled past the cap: flags, routes and per-head
-    outputs (auto equals the forced route bitwise)."""
-    w = workloads.custom("mixed_small", 2, 8, 1500, 128, "bf16", False, base="mixed")
+    """A quarter of 40 heads scaled past the cap: flags, routes and per-head
+    outputs (auto equals the forced route bitwise, also for the heads past
+    the first 32, whose last query tiles the fixed kernel does not split)."""
+    w = workloads.custom("mixed_small", 2, 20, 700, 128, "bf16", False, base="mixed")
     host, dev = _inputs(w, seed=3)
     mu, cert, ref = check_certify(clis, w, host, dev)
     fails = set(workloads.failing_heads(w, 3).tolist())
-    assert len(fails) == 4
+    assert len(fails) == 10 and min(fails) < 32 < max(fails)
     assert {i for i, c in enumerate(ref["cert"].ravel()) if not c} == fails
     run_attention(clis, w, host, dev, mu, cert)
 
@@ -279,12 +271,47 @@ def test_certified_head_near_the_cap_stays_finite(clis):
     _, mx, _ = oracle.fixed_mu_head(qd, kd, oracle.decode(host[2][0, 0], "bf16"), scale, ref["mu"][0, 0],
                                     rows=np.array([0]))
     assert mx[0] > 0.9 * ref["C"][0, 0]
-    o = clis.clis_attn_fwd(*dev, scale, mode="fixed", mu=mu)
-    torch.cuda.synchronize()
     want = oracle.attention(*host, "bf16", scale)
-    got = to_f64(o)
-    assert_valid(got, "near_cap")
-    assert_close(got, want, "bf16", "near_cap")
+    for mode in ("fixed", "auto"):
+        o = clis.clis_attn_fwd(*dev, scale, mode=mode, mu=mu, cert=cert)
+        o2 = clis.clis_attn_fwd(*dev, scale, mode=mode)
+        torch.cuda.synchronize()
+        for out in (o, o2):
+            got = to_f64(out)
+            assert_valid(got, f"near_cap/{mode}")
+            assert_close(got, want, "bf16", f"near_cap/{mode}")
+
+
+@pytest.mark.parametrize("kind", workloads.EDGE_HEADS)
+def test_edge_heads_near_the_cap(clis, kind):
+    """Certified heads whose bound sits just under the cap: a large shared
+    key offset (the case the key-mean centering exists for) and two competing
+    keys near the bound with values of opposite sign (output sensitive to any
+    exponent error), with and without an offset the query row sees.  Auto
+    and fixed mode, certificate computed inside the call or given, and the
+    log-sum-exp form: valid and within the bf16 tolerances of the oracle."""
+    import torch
+    q, k, v = workloads.edge_head(kind)
+    host = tuple(workloads.round_to_bf16_bits(a)[None, None] for a in (q, k, v))
+    dev = tuple(to_device(a, "bf16") for a in host)
+    w = workloads.custom(kind, 1, 1, q.shape[0], q.shape[1], "bf16", False, Nk=k.shape[0])
+    mu, cert, ref = check_certify(clis, w, host, dev)
+    assert ref["cert"][0, 0] == 1 and ref["bound"][0, 0] > 0.95 * ref["C"][0, 0]
+    want = oracle.attention(*host, "bf16", w.scale)
+    want_lse = oracle.lse_head(*(oracle.decode(a[0, 0], "bf16") for a in host[:2]), w.scale)
+    for mode, given in (("auto", False), ("fixed", False), ("auto", True), ("fixed", True)):
+        say("edge head", kind, mode, "given certificate" if given else "certified in the call")
+        kw = dict(mu=mu, cert=cert) if given else {}
+        o, route, lse = clis.clis_attn_fwd(*dev, w.scale, mode=mode, want_route=True, want_lse=True, **kw)
+        o2 = clis.clis_attn_fwd(*dev, w.scale, mode=mode, **kw)
+        torch.cuda.synchronize()
+        assert route.item() == 1
+        for out in (o, o2):
+            got = to_f64(out)
+            assert_valid(got, f"{kind}/{mode}")
+            assert_close(got, want, "bf16", f"{kind}/{mode}")
+        got_lse = lse.cpu().numpy().astype(np.float64)[0, 0]
+        assert np.all(np.isfinite(got_lse)) and np.abs(got_lse - want_lse).max() <= 4e-3, kind
 
 
 def test_forced_fixed_on_failing_head_is_invalid(clis):
@@ -318,22 +345,57 @@ def test_empty_and_errors_through_binding(clis):
 FULL = ["wan720p", "wan480p", "mixed", "causal"]
 
 
+def extreme_rows(q, k, keys, n):
+    """Query rows of one head whose largest logits are largest, and rows whose
+    two largest logits are closest (near ties), among the key rows `keys`
+    (q, k fp64 [N, d]): two sorted arrays of n rows each."""
+    s = q @ k[keys].T
+    top = np.sort(s, axis=1)[:, -2:]
+    big = np.argsort(-top[:, 1], kind="stable")[:n]
+    tie = np.argsort(top[:, 1] - top[:, 0], kind="stable")[:n]
+    return np.sort(big).astype(np.int64), np.sort(tie).astype(np.int64)
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_workload(clis, name):
-    """Full-size inputs: certification on every head, attention on sampled
-    rows (ends, tile edges, seeded rows) in every mode."""
+    """Full-size inputs: certification on every head, attention in every mode
+    on sampled rows of every head (both ends, edges of 64-, 128- and 256-row
+    tiles, 200 seeded rows), at the stated bf16 tolerances.  On the mixed
+    workload also, in auto mode (the online route), the 50 rows of each
+    failing head with the largest logits (stated tolerances) and the 50 rows
+    whose two largest logits are closest.  Those near-tie rows have logits
+    of ~3.6e6, where one fp32 ulp of a score is 0.25 (0.03 in log2 units after
+    the scale): the fp32 accumulation of the score product moves the weights
+    of two nearly tied keys by a few percent against the fp64 oracle, which
+    no fp32-accumulating kernel avoids.  They are checked for validity and at
+    the stated mean and rel-L2 tolerances; their largest element error is
+    reported (printed with the case), not asserted."""
     w = workloads.WORKLOADS[name]
     say("generate", name)
     host, dev = _inputs(w, seed=0)
     mu, cert, ref = check_certify(clis, w, host, dev)
-    fails = set(workloads.failing_heads(w, 0).tolist())
-    assert {i for i, c in enumerate(ref["cert"].ravel()) if not c} == fails
-    rows = workloads.sample_rows(w, n_random=16, tiles=(128,))
+    fails = workloads.failing_heads(w, 0)
+    assert {i for i, c in enumerate(ref["cert"].ravel()) if not c} == set(fails.tolist())
+    rows = workloads.sample_rows(w, n_random=200, tiles=(64, 128, 256))
     outs, errs = run_attention(clis, w, host, dev, mu, cert, rows=rows)
-    say("errors", name, errs)
+    say("errors", name, len(rows), "rows per head", errs)
     import torch
     auto = outs["auto"]
     assert bool(torch.isfinite(auto).all()) and bool((auto != 0).any()), f"{name}: invalid output"
+    for flat in fails.tolist():
+        b, h = divmod(flat, w.H)
+        qd, kd, vd = (oracle.decode(a[b, h], w.dtype) for a in host)
+        big, tie = extreme_rows(qd, kd, workloads.outlier_rows(w, b, h, 0), 50)
+        for kind, er in (("largest logits", big), ("near ties", tie)):
+            want = oracle.attention_head(qd, kd, vd, w.scale, w.causal, er)
+            got = to_f64(auto[b, h].index_select(0, torch.as_tensor(er, device=auto.device)))
+            e = errors(got, want)
+            say("extreme rows", name, (b, h), kind, len(er), e)
+            assert np.all(np.isfinite(got)), f"{name} {(b, h)} {kind}: non-finite output"
+            if kind == "largest logits":
+                assert_close(got, want, w.dtype, f"{name} failing head {(b, h)} {kind}")
+            else:
+                assert e["mean_abs"] <= 1e-3 and e["rel_l2"] <= 5e-3, (name, (b, h), kind, e)
 
 
 # ---------------------------------------------------------------- maximum size

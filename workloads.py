@@ -195,6 +195,61 @@ def sample_rows(w: Workload, n_random: int = 200, seed: int = 0, tiles=(64, 128,
     return np.array(sorted(rows), dtype=np.int64)
 
 
+EDGE_HEADS = ("offset_cap", "competing_keys", "competing_keys_offset")
+
+
+def edge_head(kind: str, seed: int = 0, nq: int = 300, nk: int = 1024, d: int = 128):
+    """Hand-built heads whose certified bound sits just under the cap, as fp32
+    [N, d] arrays (q, k, v) to be rounded to bf16 by the caller.  All the
+    constants below are exact in bf16.
+
+    offset_cap: every key is 8192 e0 +- 256 e0 (half each), so the key mean
+      is 8192 e0 and the centered keys are +-256 e0; V = 0.75 everywhere;
+      q0 = 3.578125 e0, q1 = 0.5 e1, other query rows 0.1 N(0,1).  A large
+      shared key offset with the bound c * 3.578125 * 256 = 116.8 just under
+      the cap 127 - ceil(log2 1024) - 0 = 117.
+    competing_keys: keys 0.5 N(0,1) except k5 = 227 e0 and k9 = 230 e1 (the
+      bf16 value nearest 2.71875 * 227 / 2.6875); v5 = +2.5, v9 = -2.5, other
+      values N(0,1); q0 = 2.71875 e0 + 2.6875 e1, other rows 0.1 N(0,1).
+      Row 0 weighs two keys of nearly equal score (exponents ~79) with values
+      of opposite sign, so its output is sensitive to exponent errors; the
+      bound c |q0| kappa = 112.0 is just under the cap 114.
+    competing_keys_offset: as competing_keys, with 4096 added to channel 2 of
+      every key and q0[2] = 0.5 (a shared offset the row does see).
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7_000_000, EDGE_HEADS.index(kind)])))
+    q = np.float32(0.1) * rng.standard_normal((nq, d), dtype=np.float32)
+    if kind == "offset_cap":
+        k = np.zeros((nk, d), dtype=np.float32)
+        k[:, 0] = 8192.0
+        k[: nk // 2, 0] += 256.0
+        k[nk // 2:, 0] -= 256.0
+        k = k[rng.permutation(nk)]
+        v = np.full((nk, d), 0.75, dtype=np.float32)
+        q[0] = 0.0
+        q[0, 0] = 3.578125
+        q[1] = 0.0
+        q[1, 1] = 0.5
+    elif kind in ("competing_keys", "competing_keys_offset"):
+        k = np.float32(0.5) * rng.standard_normal((nk, d), dtype=np.float32)
+        v = rng.standard_normal((nk, d), dtype=np.float32)
+        k[5] = 0.0
+        k[5, 0] = 227.0
+        k[9] = 0.0
+        k[9, 1] = 230.0
+        v[5] = 2.5
+        v[9] = -2.5
+        q[0] = 0.0
+        q[0, 0] = 2.71875
+        q[0, 1] = 2.6875
+        if kind == "competing_keys_offset":
+            k[:, 2] += np.float32(4096.0)
+            q[0, 2] = 0.5
+    else:
+        raise ValueError(kind)
+    return q, k, v
+
+
 def to_torch(a: np.ndarray, dtype: str, device: str = "cuda"):
     """Copy seeded host inputs to a torch device tensor, bytes unchanged
     (bf16 bit patterns become a bfloat16 tensor)."""
