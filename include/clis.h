@@ -155,6 +155,30 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o,
                   int mode, const float* mu, const int32_t* cert, int32_t* route_out,
                   float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the device scratch that clis_attn_fwd_noalloc uses: 128 MiB. */
+#define CLIS_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/*
+ * clis_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation, arguments and results as clis_attn_fwd, bitwise,
+ * without the ws / ws_bytes arguments.  Its scratch is a static device array
+ * of CLIS_NOALLOC_SCRATCH_BYTES inside this library, one copy per GPU, held
+ * until the process ends; its address is looked up on the first call on each
+ * device.  No allocation happens in this call.
+ *   Limit: shapes whose clis_workspace_bytes(B, H, Nq, Nk, d) exceeds
+ *   CLIS_NOALLOC_SCRATCH_BYTES are rejected with CLIS_ERR_WORKSPACE (nothing
+ *   enqueued), e.g. B*H*Nk up to about 350,000 keys at d = 128 with bf16.
+ *   Concurrency: every call on one GPU shares that GPU's scratch, which keeps
+ *   the last call's contents (each call writes everything it reads before
+ *   reading it).  Calls that overlap on one GPU -- on different streams or
+ *   from different threads without ordering -- race and must not be issued.
+ */
+int clis_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                          int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                          int mode, const float* mu, const int32_t* cert, int32_t* route_out,
+                          float* lse_out, void* stream);
+
 /*
  * Online-softmax attention forward for every head: the tuned baseline and the
  * fallback path [CLiS abstract: running row maxima and accumulator

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
     clis_certify(q, k, v, scale)       -> (mu, cert[, stats, kbar])
     clis_attn_fwd(q, k, v, ...)        -> o[, route][, lse]
                                           (mode auto/fixed/online/online_lazy)
+    clis_attn_fwd_noalloc(q, k, v, out=o, ...) -> o   (no workspace, no allocation)
     online_attn_fwd(q, k, v, ...)      -> o            (optionally with lse)
     clis_attn_fwd_partial(q, k_shard, v_shard, mu, o_acc, l_acc, ...)
     clis_attn_combine(o_acc, l_acc, ...) -> o        (optionally with lse)
@@ -34,9 +35,10 @@ CLIS_BF16, CLIS_FP32 = 0, 1
 MODES = {"auto": 0, "fixed": 1, "online": 2, "online_lazy": 3}
 STATUS = {0: "CLIS_OK", 1: "CLIS_ERR_NULL", 2: "CLIS_ERR_SHAPE", 3: "CLIS_ERR_UNSUPPORTED",
           4: "CLIS_ERR_ALIGN", 5: "CLIS_ERR_WORKSPACE", 6: "CLIS_ERR_HIP"}
-EXPORTS = ["clis_workspace_bytes", "clis_certify", "clis_attn_fwd", "online_attn_fwd",
+EXPORTS = ["clis_workspace_bytes", "clis_certify", "clis_attn_fwd", "clis_attn_fwd_noalloc", "online_attn_fwd",
            "clis_attn_fwd_partial", "clis_attn_combine", "clis_status_string", "clis_last_error",
            "clis_abi_version"]
+NOALLOC_SCRATCH_BYTES = 128 << 20  # CLIS_NOALLOC_SCRATCH_BYTES of include/clis.h
 
 # clis_head_stats_t: 4 doubles, 6 int32
 STATS_DTYPE = np.dtype([("kappa", "<f8"), ("qnorm_max", "<f8"), ("bound", "<f8"), ("maxabs_v", "<f8"),
@@ -61,11 +63,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.clis_workspace_bytes.restype = sz
     L.clis_certify.argtypes = [vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, vp, vp, sz, vp]
     L.clis_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+    L.clis_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp, vp, vp, vp]
     L.online_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, vp, sz, vp]
     L.clis_attn_fwd_partial.argtypes = [vp, vp, vp, i, i, i, i, i, f, i, i, vp, i, i, vp, vp, vp, sz, vp]
     L.clis_attn_combine.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, vp]
-    for fn in (L.clis_certify, L.clis_attn_fwd, L.online_attn_fwd, L.clis_attn_fwd_partial, L.clis_attn_combine,
-               L.clis_abi_version):
+    for fn in (L.clis_certify, L.clis_attn_fwd, L.clis_attn_fwd_noalloc, L.online_attn_fwd, L.clis_attn_fwd_partial,
+               L.clis_attn_combine, L.clis_abi_version):
         fn.restype = ctypes.c_int
     L.clis_abi_version.argtypes = []
     L.clis_status_string.argtypes = [i]
@@ -188,6 +191,22 @@ def clis_attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, mod
                              _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     res = (o,) + ((route,) if want_route else ()) + ((lse,) if want_lse else ())
     return res if len(res) > 1 else o
+
+
+def clis_attn_fwd_noalloc(q, k, v, scale: float | None = None, causal: bool = False, mode: str = "auto",
+                          mu=None, cert=None, out=None, route=None, lse=None, stream=None):
+    """clis_attn_fwd without a workspace (clis_attn_fwd_noalloc): the library's
+    static per-GPU scratch instead.  The caller passes every output tensor it
+    wants (out is required; route [B,H] int32 and lse [B,H,Nq] fp32 are
+    optional), so this call allocates nothing.  Returns out."""
+    B, H, Nq, Nk, d = _shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None or out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    _check(get_lib().clis_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Nq, Nk, d, scale,
+                                           int(causal), _dtype_code(q), MODES[mode], _ptr(mu), _ptr(cert),
+                                           _ptr(route), _ptr(lse), _stream(stream)))
+    return out
 
 
 def online_attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, want_lse: bool = False,

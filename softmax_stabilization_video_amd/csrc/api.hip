@@ -6,9 +6,40 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 namespace {
+
+// Scratch of clis_attn_fwd_noalloc, for callers that cannot allocate: one
+// copy per GPU, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: every use goes through the
+// device address that scratch_address() looks up once per device.
+__device__ __align__(256) unsigned char scratch[CLIS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's `scratch` (looked up on the first
+// call on each device, with that device current).
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 thread_local char g_err[512] = "";
 
@@ -52,6 +83,18 @@ int check_io(const void* q, const void* k, const void* v, const void* o, bool ne
   if (!q || !k || !v || (need_o && !o)) return fail(CLIS_ERR_NULL, "q, k, v%s must be non-NULL", need_o ? ", o" : "");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || (need_o && !aligned(o, 16)))
     return fail(CLIS_ERR_ALIGN, "q, k, v, o must be 16-byte aligned");
+  return CLIS_OK;
+}
+
+// Pointer checks of the attention entry points (q, k, v, o and the
+// optional per-row / per-head arrays).
+int check_attn_io(const void* q, const void* k, const void* v, const void* o, const float* mu,
+                  const int32_t* cert, const int32_t* route_out, const float* lse_out) {
+  int st = check_io(q, k, v, o, true);
+  if (st != CLIS_OK) return st;
+  if ((lse_out && !aligned(lse_out, 4)) || (mu && !aligned(mu, 4)) || (cert && !aligned(cert, 4)) ||
+      (route_out && !aligned(route_out, 4)))
+    return fail(CLIS_ERR_ALIGN, "mu, cert, route_out and lse_out must be 4-byte aligned");
   return CLIS_OK;
 }
 
@@ -149,10 +192,7 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
   bool empty = false;
   int st = check_common(B, H, Nq, Nk, d, scale, dtype, causal, &empty);
   if (st != CLIS_OK || empty) return st;
-  if ((st = check_io(q, k, v, o, true)) != CLIS_OK) return st;
-  if ((lse_out && !aligned(lse_out, 4)) || (mu && !aligned(mu, 4)) || (cert && !aligned(cert, 4)) ||
-      (route_out && !aligned(route_out, 4)))
-    return fail(CLIS_ERR_ALIGN, "mu, cert, route_out and lse_out must be 4-byte aligned");
+  if ((st = check_attn_io(q, k, v, o, mu, cert, route_out, lse_out)) != CLIS_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   clis::AttnArgs a = attn_args(q, k, v, o, B, H, Nq, Nk, d, scale, causal);
   a.lse = lse_out;
@@ -216,6 +256,28 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
     if ((e = launch_attn(g, dtype, false, vt, s)) != hipSuccess) return hip_fail(e, "online attention launch");
   }
   return CLIS_OK;
+}
+
+int clis_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int B, int H, int Nq, int Nk,
+                          int d, float scale, int causal, int dtype, int mode, const float* mu,
+                          const int32_t* cert, int32_t* route_out, float* lse_out, void* stream) {
+  g_err[0] = 0;
+  if (mode != CLIS_MODE_AUTO && mode != CLIS_MODE_FIXED && mode != CLIS_MODE_ONLINE &&
+      mode != CLIS_MODE_ONLINE_LAZY)
+    return fail(CLIS_ERR_UNSUPPORTED, "unknown mode %d", mode);
+  bool empty = false;
+  int st = check_common(B, H, Nq, Nk, d, scale, dtype, causal, &empty);
+  if (st != CLIS_OK || empty) return st;
+  if ((st = check_attn_io(q, k, v, o, mu, cert, route_out, lse_out)) != CLIS_OK) return st;
+  const size_t need = clis::ws_layout(B, H, Nq, Nk, d).total;
+  if (need > (size_t)CLIS_NOALLOC_SCRATCH_BYTES)
+    return fail(CLIS_ERR_WORKSPACE, "shape needs %zu bytes of scratch, more than the %zu of clis_attn_fwd_noalloc "
+                "(use clis_attn_fwd with a workspace)", need, (size_t)CLIS_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e, "scratch address");
+  return clis_attn_fwd(q, k, v, o, B, H, Nq, Nk, d, scale, causal, dtype, mode, mu, cert, route_out, lse_out, ws,
+                       (size_t)CLIS_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int online_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int Nq, int Nk,

@@ -92,6 +92,36 @@ def test_argument_checks_reject_before_launch(clis, case, expected):
     assert clis.lib.clis_last_error() != b""
 
 
+@pytest.mark.parametrize("case,expected", [
+    (dict(d=96), 3),
+    (dict(mode=7), 3),
+    (dict(o=None), 1),
+    (dict(q=0x10004), 4),
+    (dict(lse=0x60002), 4),
+    (dict(Nq=10, Nk=12, causal=1), 2),
+    (dict(H=12, Nq=40000, Nk=40000, d=128), 5),   # workspace beyond the static scratch
+])
+def test_noalloc_argument_checks(clis, case, expected):
+    """clis_attn_fwd_noalloc rejects bad calls, and shapes whose workspace
+    exceeds its static scratch, before any HIP call (CPU only)."""
+    a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, B=1, H=2, Nq=10, Nk=10, d=64, causal=0, mode=0,
+             lse=None)
+    a.update(case)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = clis.lib.clis_attn_fwd_noalloc(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), a["B"], a["H"], a["Nq"],
+                                        a["Nk"], a["d"], 0.125, a["causal"], 0, a["mode"], None, None, None,
+                                        vp(a["lse"]), None)
+    assert st == expected, clis.lib.clis_last_error()
+    if expected == 5:
+        assert b"scratch" in clis.lib.clis_last_error()
+
+
+def test_noalloc_scratch_constant_matches_header(clis):
+    text = open(HEADER).read()
+    m = re.search(r"#define CLIS_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == clis.NOALLOC_SCRATCH_BYTES
+
+
 def test_empty_batch_is_a_no_op(clis):
     # nothing to compute: CLIS_OK without touching any pointer
     for B, H, Nq in ((0, 4, 10), (2, 0, 10), (2, 4, 0)):
@@ -102,6 +132,8 @@ def test_empty_batch_is_a_no_op(clis):
         assert clis.lib.clis_attn_fwd_partial(None, None, None, B, H, Nq, 10, 128, 0.1, 0, 0, None, 0, 0, None,
                                               None, None, 0, None) == 0
         assert clis.lib.clis_attn_combine(None, None, None, B, H, Nq, 128, 0, None, None, None) == 0
+        assert clis.lib.clis_attn_fwd_noalloc(None, None, None, None, B, H, Nq, 10, 128, 0.1, 0, 0, 0, None, None,
+                                              None, None, None) == 0
         assert clis.lib.clis_certify(None, None, None, B, H, Nq, 10, 128, 0.1, 0, None, None, None, None,
                                      None, 0, None) == 0
 
