@@ -42,7 +42,8 @@ def dominant_kernel(w):
     """(name, source) of the fixed-stabilizer kernel that runs this workload."""
     c = "true" if w.causal else "false"
     if w.dtype == "bf16":
-        return f"attn_fwd_bf16<{w.d}, true, {c}, 8, false, false>", os.path.join(CSRC, "attn_bf16.hip")
+        h = 2 if w.d == 128 else 1  # row halves per wave of the fixed kernel that returns O
+        return f"attn_fwd_bf16<{w.d}, true, {c}, 8, false, false, {h}>", os.path.join(CSRC, "attn_bf16.hip")
     return f"attn_fwd_fp32<{w.d}, true, {c}, false>", os.path.join(CSRC, "attn_fp32.hip")
 
 

@@ -36,7 +36,7 @@ struct WsLayout {
   size_t cert;       // [BH]        int32
   size_t lists;      // [2][BH]     int32  heads routed fixed / online
   size_t counts;     // [8]         int32  list lengths, work counters, split heads
-  size_t vt;         // [BH][d][Nk_pad] bf16  V^T for the bf16 attention kernels
+  size_t vt;         // [BH][Nk_pad / 64][d][kVtRow] bf16  V^T tiles for the bf16 attention kernels
   size_t vmax_blk;   // [BH][vt_pad(Nk) / 64] fp32  max |V| per 64-key block, from the V transpose
   size_t tail_o;     // [kTailSlots][kTailRows][d] fp32  key-split partial sums of the pool
   size_t tail_l;     // [kTailSlots][kTailRows]    fp32
@@ -49,14 +49,19 @@ struct WsLayout {
 // kTailSplits key splits are the last query tiles of the heads with index
 // below kSplitHeads that the kernel runs: a function of the head alone, so a
 // head's result does not depend on which other heads are routed with it.
-constexpr int kTailSlots = 256;
-constexpr int kTailRows = 256;
+constexpr int kTailSlots = 128;
+constexpr int kTailRows = 512;
 constexpr int kPoolWorkers = 256;
 constexpr int kTailSplits = 8;
 constexpr int kSplitHeads = kTailSlots / kTailSplits;
 
 // Keys of the V^T copy, padded to whole 128-key tiles (either tile size).
 inline int vt_pad(int Nk) { return (Nk + 127) / 128 * 128; }
+// The V^T copy is stored as 64-key tiles, each d rows (channels) of kVtRow
+// bf16: the tile's 64 keys, then 8 zeros.  A tile is then one contiguous
+// block laid out exactly as the kernels keep it in LDS.
+constexpr int kVtRow = 72;
+inline size_t vt_bytes(int BH, int Nk, int d) { return (size_t)BH * (vt_pad(Nk) / 64) * d * kVtRow * 2; }
 
 inline WsLayout ws_layout(int B, int H, int Nq, int Nk, int d) {
   const size_t BH = (size_t)B * H, Sk = cert_splits(Nk), Sq = cert_splits(Nq);
@@ -72,7 +77,7 @@ inline WsLayout ws_layout(int B, int H, int Nq, int Nk, int d) {
   w.cert = o;      o = align256(o + BH * sizeof(int32_t));
   w.lists = o;     o = align256(o + 2 * BH * sizeof(int32_t));
   w.counts = o;    o = align256(o + 8 * sizeof(int32_t));
-  w.vt = o;        o = align256(o + BH * (size_t)d * vt_pad(Nk) * 2);
+  w.vt = o;        o = align256(o + vt_bytes((int)BH, Nk, d));
   w.vmax_blk = o;  o = align256(o + BH * (size_t)(vt_pad(Nk) / 64) * sizeof(float));
   w.tail_o = o;    o = align256(o + (size_t)kTailSlots * kTailRows * d * sizeof(float));
   w.tail_l = o;    o = align256(o + (size_t)kTailSlots * kTailRows * sizeof(float));
@@ -127,8 +132,8 @@ struct AttnArgs {
   const int32_t* split_heads = nullptr;  // device count of listed heads < kSplitHeads
 };
 
-// bf16 kernels: V is read through a transposed copy [BH][d][vt_pad(Nk)]
-// that launch_transpose_v writes.
+// bf16 kernels: V is read through a transposed copy [BH][vt_pad(Nk) / 64]
+// [d][kVtRow] that launch_transpose_v writes.
 // vmax_blk (or NULL): also writes max |V| of every 64-key block, [BH][vt_pad(Nk) / 64].
 hipError_t launch_transpose_v(const void* v, void* vt, int BH, int Nk, int d, hipStream_t s,
                               float* vmax_blk = nullptr);

@@ -1,10 +1,13 @@
 // transpose.hip -- the V^T copy that the bf16 attention kernels read their
 // P.V operands from (layout: see the V^T paragraph of attn_bf16.hip).
 //
-// V [BH][Nk][D] -> V^T [BH][D][Nk_pad] bf16, Nk_pad = vt_pad(Nk), zeros past
-// the last key, and within every 16-key group the keys stored in the order
-// {0-3, 8-11, 4-7, 12-15} (vt_pos): a lane's P.V operand, keys 4g..4g+3 and
-// 8+4g..8+4g+3 of a 16-key step (g = lane / 32), is then contiguous.
+// V [BH][Nk][D] -> V^T tiles [BH][Nk_pad / 64][D][kVtRow] bf16, Nk_pad =
+// vt_pad(Nk): row c of tile t holds channel c of keys 64t .. 64t + 63, zeros
+// past the last key, then 8 zeros of padding (the kernels' LDS row stride, so
+// a tile loads into LDS as one contiguous copy).  Within every 16-key group
+// the keys are stored in the order {0-3, 8-11, 4-7, 12-15} (vt_pos): a lane's
+// P.V operand, keys 4g..4g+3 and 8+4g..8+4g+3 of a 16-key step (g = lane /
+// 32), is then contiguous.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -25,12 +28,12 @@ __device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1)
 // read V again.
 template <int D>
 __global__ void __launch_bounds__(256)
-transpose_v(const uint16_t* __restrict__ V, uint16_t* __restrict__ Vt, int Nk, int Nk_pad, int nblk,
+transpose_v(const uint16_t* __restrict__ V, uint16_t* __restrict__ Vt, int Nk, int nblk,
             float* __restrict__ vmax_blk) {
   __shared__ uint16_t t[D][kTK + 2];  // [channel][key position]; +2 breaks bank strides
   const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk, kt = blk * kTK;
   const uint16_t* src = V + (size_t)bh * Nk * D;
-  uint16_t* dst = Vt + (size_t)bh * D * Nk_pad;
+  uint16_t* dst = Vt + (size_t)blockIdx.x * D * kVtRow;  // tile blk of head bh
   constexpr int CPR = D / 8;
   float vmax = 0.f;
   for (int i = threadIdx.x; i < kTK * CPR; i += 256) {
@@ -68,12 +71,16 @@ transpose_v(const uint16_t* __restrict__ V, uint16_t* __restrict__ Vt, int Nk, i
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < D * (kTK / 8); i += 256) {
-    const int c = i / (kTK / 8), q = i % (kTK / 8);
-    uint32_t w[4];
+  constexpr int QPR = kVtRow / 8;  // 16-byte pieces per tile row, the last one padding
+  static_assert(kVtRow == kTK + 8, "a V^T tile row: the block's keys and one 16-byte pad");
+  for (int i = threadIdx.x; i < D * QPR; i += 256) {
+    const int c = i / QPR, q = i % QPR;
+    uint32_t w[4] = {0, 0, 0, 0};
+    if (q < kTK / 8) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)t[c][q * 8 + 2 * e] | ((uint32_t)t[c][q * 8 + 2 * e + 1] << 16);
-    *reinterpret_cast<uint4*>(dst + (size_t)c * Nk_pad + kt + q * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int e = 0; e < 4; ++e) w[e] = (uint32_t)t[c][q * 8 + 2 * e] | ((uint32_t)t[c][q * 8 + 2 * e + 1] << 16);
+    }
+    *reinterpret_cast<uint4*>(dst + i * 8) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -85,8 +92,8 @@ hipError_t launch_transpose_v(const void* v, void* vt, int BH, int Nk, int d, hi
   if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const uint16_t* src = static_cast<const uint16_t*>(v);
   uint16_t* dst = static_cast<uint16_t*>(vt);
-  if (d == 128) transpose_v<128><<<(unsigned)blocks, 256, 0, s>>>(src, dst, Nk, vt_pad(Nk), nblk, vmax_blk);
-  else if (d == 64) transpose_v<64><<<(unsigned)blocks, 256, 0, s>>>(src, dst, Nk, vt_pad(Nk), nblk, vmax_blk);
+  if (d == 128) transpose_v<128><<<(unsigned)blocks, 256, 0, s>>>(src, dst, Nk, nblk, vmax_blk);
+  else if (d == 64) transpose_v<64><<<(unsigned)blocks, 256, 0, s>>>(src, dst, Nk, nblk, vmax_blk);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
