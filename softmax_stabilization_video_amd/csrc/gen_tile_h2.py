@@ -17,7 +17,8 @@ block kb:
           (round to nearest even) packed in place;
   pv<kb>  output O_h^T += V^T_kb P_h^T: 16 MFMAs, each V^T fragment read from
           LDS feeds both halves; between them the row sums l_h += the bf16
-          weights (v_dot2c with (1, 1)).
+          weights, unpacked and added in fp32 (a v_dot2 between products
+          would hold the matrix pipeline: about 18 cycles each on gfx950).
 The two waves of a SIMD run the chain half a tile apart: in the window
 between two barriers the first wave runs pv1' qk0 sm0 pv0 qk1 sm1 and the
 second sm1' pv1' qk0 sm0 pv0 qk1 (' = the previous tile's part), so that one
@@ -260,8 +261,18 @@ def generate(parts, tag):
                  [base + 2 * e, base + 2 * e + 1], [base + e]) for e in range(8)]
 
     def sums(h):
-        base = S(h)
-        return [(f"v_dot2c_f32_bf16 %[l{h}], 0x3f803f80, v{base + e}", [base + e], []) for e in range(8)]
+        # l_h += the two bf16 weights of each packed register, low then high,
+        # as fp32 adds (a v_dot2 between products holds the matrix pipeline,
+        # about 18 cycles each on gfx950); the unpacked values go through
+        # S_h's registers 8 and 9, free once P is packed
+        base, ta, tb = S(h), S(h) + 8, S(h) + 9
+        ops = []
+        for e in range(8):
+            ops += [(f"v_lshlrev_b32 v{ta}, 16, v{base + e}", [base + e], [ta]),
+                    (f"v_and_b32 v{tb}, 0xffff0000, v{base + e}", [base + e], [tb]),
+                    (f"v_add_f32 %[l{h}], v{ta}, %[l{h}]", [ta], []),
+                    (f"v_add_f32 %[l{h}], v{tb}, %[l{h}]", [tb], [])]
+        return ops
 
     for p in parts:
         kb, prev = int(p[2]), p.endswith("p")
@@ -277,8 +288,10 @@ def generate(parts, tag):
                 for h in range(2):
                     dst = f"v[{S(h)}:{S(h) + 15}]"
                     c = "0" if st == 0 else dst
+                    # (st = 0: its result overwrites registers the row sums
+                    # used; the wait covers that write after VALU writes)
                     q = g.mfma(dst, f"v[{FB + 4 * j}:{FB + 4 * j + 3}]", f"%[q{h}{st}]", c,
-                               [FB + 4 * j + i for i in range(4)])
+                               [FB + 4 * j + i for i in range(4)] + ([S(h) + r for r in range(16)] if st == 0 else []))
                     for r in range(16):
                         g.ready_valu[S(h) + r] = q + HZ_MFMA_VALU
                     g.use_frag(fid)
@@ -313,7 +326,7 @@ def generate(parts, tag):
                                f"%[o{h}{c}]", [FB + 4 * j + i for i in range(4)] + [pb + i for i in range(4)])
                         g.use_frag(fid)
                         refill()
-                        drain_some(1)
+                        drain_some(4)
                         after_mfma()
             while valu_q:
                 g.valu(*valu_q.pop(0))
