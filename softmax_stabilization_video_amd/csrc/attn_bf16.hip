@@ -498,16 +498,23 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
     return key < nkl && (!CAUSAL || kv_offset + key <= qrow[h]);
   };
-  // bf16 weights of one block packed for the product; the row sum adds the
-  // same rounded weights (v_dot2 with (1, 1): it holds the matrix pipeline
-  // while it runs, but in compiled code it measured faster than four plain
-  // VALU ops a pair)
+  // bf16 weights of one block packed for the product, and the row sum.  The
+  // fixed forms add the fp32 weights, register by register (as the
+  // generated two-half code does, so that a one-shard call is bitwise the
+  // dense fixed call); the online forms add the rounded weights with v_dot2
+  // (which holds the matrix pipeline while it runs, but measured faster in
+  // this compiled code than plain adds)
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   auto pack = [&](const float* p, uint32_t* pw, int h) {
+    if constexpr (FIXED) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lsum[h] += p[r];
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       pw[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
-      lsum[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), ones, lsum[h], false);
+      if constexpr (!FIXED)
+        lsum[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), ones, lsum[h], false);
     }
   };
   // O^T += V^T P^T for one 32-key block

@@ -13,12 +13,12 @@ block kb:
           keeps every fragment read two pairs of products ahead with a ring
           of three);
   sm<kb>  weights x = fma(s, c, -mu_h); p = exp2(x); masked keys (tail,
-          causal) get p = 0 under a branch on a uniform flag; p -> bf16
-          (round to nearest even) packed in place;
+          causal) get p = 0 under a branch on a uniform flag; the row sums
+          l_h += p in fp32; p -> bf16 (round to nearest even) packed in place;
   pv<kb>  output O_h^T += V^T_kb P_h^T: 16 MFMAs, each V^T fragment read from
-          LDS feeds both halves; between them the row sums l_h += the bf16
-          weights, unpacked and added in fp32 (a v_dot2 between products
-          would hold the matrix pipeline: about 18 cycles each on gfx950).
+          LDS feeds both halves, and no VALU between them (a v_dot2 row sum
+          there would hold the matrix pipeline: about 18 cycles each on
+          gfx950).
 The two waves of a SIMD run the chain half a tile apart: in the window
 between two barriers the first wave runs pv1' qk0 sm0 pv0 qk1 sm1 and the
 second sm1' pv1' qk0 sm0 pv0 qk1 (' = the previous tile's part), so that one
@@ -261,18 +261,12 @@ def generate(parts, tag):
                  [base + 2 * e, base + 2 * e + 1], [base + e]) for e in range(8)]
 
     def sums(h):
-        # l_h += the two bf16 weights of each packed register, low then high,
-        # as fp32 adds (a v_dot2 between products holds the matrix pipeline,
-        # about 18 cycles each on gfx950); the unpacked values go through
-        # S_h's registers 8 and 9, free once P is packed
-        base, ta, tb = S(h), S(h) + 8, S(h) + 9
-        ops = []
-        for e in range(8):
-            ops += [(f"v_lshlrev_b32 v{ta}, 16, v{base + e}", [base + e], [ta]),
-                    (f"v_and_b32 v{tb}, 0xffff0000, v{base + e}", [base + e], [tb]),
-                    (f"v_add_f32 %[l{h}], v{ta}, %[l{h}]", [ta], []),
-                    (f"v_add_f32 %[l{h}], v{tb}, %[l{h}]", [tb], [])]
-        return ops
+        # l_h += the fp32 weights of the block (after masking, before the
+        # bf16 packs), one dependent add each: the row sum is built in the
+        # weights phase and the products phase carries no VALU (a v_dot2
+        # would hold the matrix pipeline)
+        base = S(h)
+        return [(f"v_add_f32 %[l{h}], v{base + r}, %[l{h}]", [base + r], []) for r in range(16)]
 
     for p in parts:
         kb, prev = int(p[2]), p.endswith("p")
@@ -308,13 +302,15 @@ def generate(parts, tag):
                 g.pad(max(g.ready_valu.get(S(h) + r, 0) for r in range(16)))
                 for line in mask(kb, h, prev):
                     g.emit(line, 0 if line.endswith(":") else 1)
+            for a, b in zip(sums(0), sums(1)):  # the halves' chains alternate
+                g.valu(*a)
+                g.valu(*b)
+            for h in range(2):
                 for op in packs(h):
                     g.valu(*op)
         else:
-            # output products: each V^T fragment feeds both halves; the row
-            # sums of this block go between them
+            # output products: each V^T fragment feeds both halves
             assert not valu_q
-            valu_q.extend(sums(0) + sums(1))
             for t in range(2):
                 for c in range(NC):
                     fid = frag_v(kb, t, c, prev)
@@ -326,7 +322,6 @@ def generate(parts, tag):
                                f"%[o{h}{c}]", [FB + 4 * j + i for i in range(4)] + [pb + i for i in range(4)])
                         g.use_frag(fid)
                         refill()
-                        drain_some(4)
                         after_mfma()
             while valu_q:
                 g.valu(*valu_q.pop(0))

@@ -17,8 +17,8 @@ kernel can form x from bf16 inputs:
             every exponent by (q' - c q).k_j: unbounded through the shared key
             offset kbar, and up to 2^-9 B_h through the centered keys.
 
-then weights 2^x in fp32, rounded to bf16 for the P.V product, row sums of the
-rounded weights in fp32, and O = sum p v / l.  The kept form must match the
+then weights 2^x in fp32, row sums of those fp32 weights, the weights rounded
+to bf16 for the P.V product, and O = sum p v / l.  The kept form must match the
 oracle within the bf16 tolerances on every edge head; the shortcut fails both
 ways on them (NaN from overflow on a certified head with a large key offset,
 an error of ~0.4 on one with two competing keys near the bound), which is why
@@ -63,8 +63,9 @@ def emulate_fixed(q, k, v, mu, form):
     else:
         raise ValueError(form)
     with np.errstate(over="ignore", invalid="ignore"):
-        p = _bf16(np.exp2(x))  # v_exp_f32, then bf16 for the P.V operand
-        l = p.sum(axis=1, dtype=np.float32)
+        p32 = np.exp2(x).astype(np.float32)  # v_exp_f32
+        l = p32.sum(axis=1, dtype=np.float32)  # row sums of the fp32 weights
+        p = _bf16(p32)  # bf16 for the P.V operand
         acc = (p.astype(np.float64) @ v.astype(np.float64))
         acc = np.where(np.isfinite(acc) & (np.abs(acc) < np.finfo(np.float32).max), acc, np.inf * np.sign(acc))
         o = acc.astype(np.float32) / l[:, None]
