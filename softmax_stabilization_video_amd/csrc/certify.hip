@@ -16,6 +16,8 @@
 //   3. cert_norms: key splits -> partial max ||k - kbar||^2 (steps 2-3);
 //      query splits -> partial max ||q||^2 and mu_r = c (q_r . kbar)
 //   4. cert_finalize: kappa, B_h, G, A, C, flag per head         (steps 3-7)
+// With one key split and one query split (short sequences) cert_small runs
+// the four passes for a head in one block: one launch instead of four.
 // Every reduction has a fixed order (no atomics), so results are bitwise
 // reproducible.  Maxima propagate NaN so that a NaN input never certifies.
 #include <hip/hip_runtime.h>
@@ -43,8 +45,9 @@ __device__ __forceinline__ double to_f64(uint16_t b) {
 }
 __device__ __forceinline__ double to_f64(float f) { return (double)f; }
 
-// Rows in flight per lane in the streaming loops (loads issued before use).
-constexpr int kUnroll = 4;
+// Rows in flight per lane in the streaming loops (loads issued before use):
+// enough that a CU keeps 64 KB or more of reads outstanding.
+constexpr int kUnroll = 8;
 
 // 16 bytes of row elements, widened to fp64.
 template <typename T>
@@ -86,44 +89,45 @@ __device__ double block_max(double x, double* red) {
 }
 
 // Step 1 (partial column sums of K) and step 5 (partial max |V|).
-template <typename T, int D>
-__global__ void __launch_bounds__(kThreads)
-cert_keys_values(const T* __restrict__ K, const T* __restrict__ V, int Nk, int Sk,
-                 double* __restrict__ ksum_part, double* __restrict__ vmax_part) {
+// (one block: head bh, key split `split`)
+template <typename T, int D, bool WITH_V>
+__device__ __forceinline__ void keys_values_block(const T* __restrict__ K, const T* __restrict__ V, int Nk, int Sk,
+                                                  double* __restrict__ ksum_part, double* __restrict__ vmax_part,
+                                                  int bh, int split) {
   constexpr int VEC = Vec<T>::n, TPR = D / VEC, RPI = kThreads / TPR;
   __shared__ double colsum[RPI][D];
   __shared__ double red[kThreads / 64];
-  const int bh = blockIdx.x / Sk, split = blockIdx.x % Sk;  // 1-D grid: any head count
   int lo, hi;
   split_range(Nk, Sk, split, &lo, &hi);
   const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
   const T* kb = K + (size_t)bh * Nk * D;
-  const T* vb = V ? V + (size_t)bh * Nk * D : nullptr;  // NULL: max |V| comes from the transpose
+  const T* vb = WITH_V ? V + (size_t)bh * Nk * D : nullptr;  // without: max |V| comes from the transpose
   double acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
   double vmax = 0.0;
-  // kUnroll rows per lane in flight; the sums still run in row order
-  for (int j0 = lo + tr; j0 < hi; j0 += kUnroll * RPI) {
-    uint4 uk[kUnroll], uv[kUnroll];
+  // UN rows per lane in flight; the sums still run in row order
+  constexpr int UN = WITH_V ? kUnroll / 2 : kUnroll;
+  for (int j0 = lo + tr; j0 < hi; j0 += UN * RPI) {
+    uint4 uk[UN], uv[WITH_V ? UN : 1];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < UN; ++u) {
       const int j = j0 + u * RPI;
       uk[u] = make_uint4(0, 0, 0, 0);
-      uv[u] = make_uint4(0, 0, 0, 0);
+      if constexpr (WITH_V) uv[u] = make_uint4(0, 0, 0, 0);
       if (j < hi) {
         uk[u] = *reinterpret_cast<const uint4*>(kb + (size_t)j * D + tc * VEC);
-        if (vb) uv[u] = *reinterpret_cast<const uint4*>(vb + (size_t)j * D + tc * VEC);
+        if constexpr (WITH_V) uv[u] = *reinterpret_cast<const uint4*>(vb + (size_t)j * D + tc * VEC);
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < UN; ++u) {
       if (j0 + u * RPI >= hi) break;
       double x[VEC];
       widen<T>(uk[u], x);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) acc[e] += x[e];
-      if (vb) {
+      if constexpr (WITH_V) {
         widen<T>(uv[u], x);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) vmax = max_keep_nan(vmax, fabs(x[e]));
@@ -142,18 +146,28 @@ cert_keys_values(const T* __restrict__ K, const T* __restrict__ V, int Nk, int S
   if (threadIdx.x == 0) vmax_part[(size_t)bh * Sk + split] = vmax;
 }
 
-// Step 1: kbar from the split partials, summed in split order.
+template <typename T, int D, bool WITH_V>
+__global__ void __launch_bounds__(kThreads)
+cert_keys_values(const T* __restrict__ K, const T* __restrict__ V, int Nk, int Sk,
+                 double* __restrict__ ksum_part, double* __restrict__ vmax_part) {
+  // 1-D grid: any head count
+  keys_values_block<T, D, WITH_V>(K, V, Nk, Sk, ksum_part, vmax_part, blockIdx.x / Sk, blockIdx.x % Sk);
+}
+
+// Step 1: kbar from the split partials, summed in split order (threads c <
+// D of the block; every thread reaches the barrier).
 template <int D>
-__global__ void __launch_bounds__(D)
-cert_kbar(const double* __restrict__ ksum_part, int Nk, int Sk, double* __restrict__ kbar,
-          const float* __restrict__ vmax_blk, int nblk, double* __restrict__ vmax_part) {
-  const int bh = blockIdx.x, c = threadIdx.x;
+__device__ __forceinline__ void kbar_block(const double* __restrict__ ksum_part, int Nk, int Sk,
+                                           double* __restrict__ kbar, const float* __restrict__ vmax_blk, int nblk,
+                                           double* __restrict__ vmax_part, int bh) {
+  const int c = threadIdx.x;
   if (vmax_blk) {  // block maxima of |V| from the transpose -> split 0's partial
     __shared__ double red[(D + 63) / 64];
     double m = 0.0;
-    for (int i = c; i < nblk; i += D) m = max_keep_nan(m, (double)vmax_blk[(size_t)bh * nblk + i]);
+    if (c < D)
+      for (int i = c; i < nblk; i += D) m = max_keep_nan(m, (double)vmax_blk[(size_t)bh * nblk + i]);
     for (int off = 32; off > 0; off >>= 1) m = max_keep_nan(m, __shfl_xor(m, off));
-    if ((c & 63) == 0) red[c >> 6] = m;
+    if (c < D && (c & 63) == 0) red[c >> 6] = m;
     __syncthreads();
     if (c == 0) {
       double r = red[0];
@@ -161,103 +175,118 @@ cert_kbar(const double* __restrict__ ksum_part, int Nk, int Sk, double* __restri
       vmax_part[(size_t)bh * Sk] = r;
     }
   }
-  const double* p = ksum_part + (size_t)bh * Sk * D + c;
-  double s = 0.0;
-  for (int i = 0; i < Sk; ++i) s += p[(size_t)i * D];
-  kbar[(size_t)bh * D + c] = s / (double)Nk;
+  if (c < D) {
+    const double* p = ksum_part + (size_t)bh * Sk * D + c;
+    double s = 0.0;
+    for (int i = 0; i < Sk; ++i) s += p[(size_t)i * D];
+    kbar[(size_t)bh * D + c] = s / (double)Nk;
+  }
 }
 
-// Sum over the TPR consecutive lanes that hold one row, in a fixed xor order.
-template <int TPR>
-__device__ __forceinline__ double row_sum(double x) {
-#pragma unroll
-  for (int off = 1; off < TPR; off <<= 1) x += __shfl_xor(x, off);
+template <int D>
+__global__ void __launch_bounds__(D)
+cert_kbar(const double* __restrict__ ksum_part, int Nk, int Sk, double* __restrict__ kbar,
+          const float* __restrict__ vmax_blk, int nblk, double* __restrict__ vmax_part) {
+  kbar_block<D>(ksum_part, Nk, Sk, kbar, vmax_blk, nblk, vmax_part, blockIdx.x);
+}
+
+// One fp64 value from another lane of the same row of 16 lanes (a DPP move
+// of both halves; the pattern CTRL never selects a lane outside the row).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+// Sum over the 8 consecutive lanes that hold one row: pairs (xor 1), quads
+// (xor 2), then the two quads (lane i with 7 - i); every lane of the group
+// ends with the same value.  DPP moves stay in the VALU.
+__device__ __forceinline__ double row8_sum(double x) {
+  x += dpp_f64<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f64<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f64<0x141>(x);  // row_half_mirror
   return x;
 }
 
 // Steps 2-3 on key splits; ||q||^2 and the stabilizers on query splits.
+// Eight lanes hold a row: lane t of the group its 16-byte chunks t, t + 8,
+// ... (contiguous 128 bytes of the row per load across the group).
+template <typename T, int D>
+__device__ __forceinline__ void norms_block(const T* __restrict__ Q, const T* __restrict__ K,
+                                            const double* __restrict__ kbar, int Nq, int Nk, int Sk, int Sq,
+                                            double c2, float* __restrict__ mu, double* __restrict__ kap_part,
+                                            double* __restrict__ qss_part, int bh, int part) {
+  constexpr int VEC = Vec<T>::n, TPR = 8, RPI = kThreads / TPR;
+  constexpr int NL = D / VEC / TPR;  // 16-byte loads per lane per row
+  constexpr int UN = NL > 2 ? kUnroll / 2 : kUnroll;  // rows per lane in flight
+  static_assert(D % (VEC * TPR) == 0, "whole chunks per lane");
+  __shared__ double red[kThreads / 64];
+  const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
+  double kb[NL][VEC];
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) kb[i][e] = kbar[(size_t)bh * D + (tc + TPR * i) * VEC + e];
+  double best = 0.0;
+  const bool keys = part < Sk;
+  const int split = keys ? part : part - Sk;
+  const int n = keys ? Nk : Nq;
+  int lo, hi;
+  split_range(n, keys ? Sk : Sq, split, &lo, &hi);
+  const T* base = (keys ? K : Q) + (size_t)bh * n * D;
+  // every lane of a row group runs the same trip count, so the DPP partners
+  // are always active
+  for (int j0 = lo; j0 < hi; j0 += UN * RPI) {
+    uint4 ld[UN][NL];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int j = j0 + u * RPI + tr;
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        ld[u][i] = j < hi ? *reinterpret_cast<const uint4*>(base + (size_t)j * D + (tc + TPR * i) * VEC)
+                          : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int j = j0 + u * RPI + tr;
+      double ss = 0.0, dot = 0.0;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        double x[VEC];
+        widen<T>(ld[u][i], x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          if (keys) {
+            const double t = x[e] - kb[i][e];
+            ss += t * t;
+          } else {
+            ss += x[e] * x[e];
+            dot += x[e] * kb[i][e];
+          }
+        }
+      }
+      ss = row8_sum(ss);
+      if (!keys) dot = row8_sum(dot);
+      if (j < hi) {
+        best = max_keep_nan(best, ss);
+        if (!keys && tc == 0) mu[(size_t)bh * Nq + j] = (float)(c2 * dot);
+      }
+    }
+  }
+  best = block_max(best, red);
+  if (threadIdx.x == 0) (keys ? kap_part[(size_t)bh * Sk + split] : qss_part[(size_t)bh * Sq + split]) = best;
+}
+
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads)
 cert_norms(const T* __restrict__ Q, const T* __restrict__ K, const double* __restrict__ kbar,
            int Nq, int Nk, int Sk, int Sq, double c2, float* __restrict__ mu,
            double* __restrict__ kap_part, double* __restrict__ qss_part) {
-  constexpr int VEC = Vec<T>::n, TPR = D / VEC, RPI = kThreads / TPR;
-  __shared__ double red[kThreads / 64];
-  const int bh = blockIdx.x / (Sk + Sq), part = blockIdx.x % (Sk + Sq);  // 1-D grid: any head count
-  const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
-  double kb[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) kb[e] = kbar[(size_t)bh * D + tc * VEC + e];
-  double best = 0.0;
-  if (part < Sk) {
-    const int split = part;
-    int lo, hi;
-    split_range(Nk, Sk, split, &lo, &hi);
-    const T* base = K + (size_t)bh * Nk * D;
-    // every lane of a row group runs the same trip count, so the shuffles
-    // inside row_sum always see their partners
-    for (int j0 = lo; j0 < hi; j0 += kUnroll * RPI) {
-      uint4 uk[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int j = j0 + u * RPI + tr;
-        uk[u] = j < hi ? *reinterpret_cast<const uint4*>(base + (size_t)j * D + tc * VEC) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int j = j0 + u * RPI + tr;
-        double ss = 0.0;
-        if (j < hi) {
-          double x[VEC];
-          widen<T>(uk[u], x);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            const double t = x[e] - kb[e];
-            ss += t * t;
-          }
-        }
-        ss = row_sum<TPR>(ss);
-        if (j < hi) best = max_keep_nan(best, ss);
-      }
-    }
-    best = block_max(best, red);
-    if (threadIdx.x == 0) kap_part[(size_t)bh * Sk + split] = best;
-  } else {
-    const int split = part - Sk;
-    int lo, hi;
-    split_range(Nq, Sq, split, &lo, &hi);
-    const T* base = Q + (size_t)bh * Nq * D;
-    for (int r0 = lo; r0 < hi; r0 += kUnroll * RPI) {
-      uint4 uq[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int r = r0 + u * RPI + tr;
-        uq[u] = r < hi ? *reinterpret_cast<const uint4*>(base + (size_t)r * D + tc * VEC) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int r = r0 + u * RPI + tr;
-        double ss = 0.0, dot = 0.0;
-        if (r < hi) {
-          double x[VEC];
-          widen<T>(uq[u], x);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            ss += x[e] * x[e];
-            dot += x[e] * kb[e];
-          }
-        }
-        ss = row_sum<TPR>(ss);
-        dot = row_sum<TPR>(dot);
-        if (r < hi) {
-          best = max_keep_nan(best, ss);
-          if (tc == 0) mu[(size_t)bh * Nq + r] = (float)(c2 * dot);
-        }
-      }
-    }
-    best = block_max(best, red);
-    if (threadIdx.x == 0) qss_part[(size_t)bh * Sq + split] = best;
-  }
+  // 1-D grid: any head count
+  norms_block<T, D>(Q, K, kbar, Nq, Nk, Sk, Sq, c2, mu, kap_part, qss_part, blockIdx.x / (Sk + Sq),
+                    blockIdx.x % (Sk + Sq));
 }
 
 // ceil(log2 x) for finite x >= 1, exactly.
@@ -267,45 +296,76 @@ __device__ __forceinline__ int ceil_log2_f64(double x) {
   return (f == 0.5) ? e - 1 : e;
 }
 
-// Steps 3-7 and the flag, one thread per head.
+// Steps 3-7 and the flag for head h (one thread).
+__device__ __forceinline__ void finalize_head(const double* __restrict__ vmax_part,
+                                              const double* __restrict__ kap_part,
+                                              const double* __restrict__ qss_part, int Nk, int Sk, int Sq,
+                                              double c2, int32_t* __restrict__ cert,
+                                              clis_head_stats_t* __restrict__ stats, int h) {
+  double vmax = 0.0, kap2 = 0.0, qss = 0.0;
+  for (int i = 0; i < Sk; ++i) {
+    vmax = max_keep_nan(vmax, vmax_part[(size_t)h * Sk + i]);
+    kap2 = max_keep_nan(kap2, kap_part[(size_t)h * Sk + i]);
+  }
+  for (int i = 0; i < Sq; ++i) qss = max_keep_nan(qss, qss_part[(size_t)h * Sq + i]);
+  const double kappa = sqrt(kap2);
+  const double qmax = sqrt(qss);
+  const double bound = (c2 * qmax) * kappa;
+  // step 5; a non-finite max |V| gets G = 128 so that C < 0
+  const int G = isfinite(vmax) ? ceil_log2_f64(vmax > 1.0 ? vmax : 1.0) : 128;
+  // step 6: ceil(log2 Nk) for Nk >= 1
+  const int L = (Nk <= 1) ? 0 : 32 - __clz(Nk - 1);
+  const int A = L + G;
+  // step 7 with the Figure 3 limits of fp32 accumulators and bf16/fp32 exp2
+  // outputs: log2 of the largest finite value is 127.99... in both formats,
+  // so floor(U_exp) = 127 and ceil(U_acc - A) - 1 = 127 - A for integer A.
+  const int C = min(127, 127 - A);
+  const int ok = (isfinite(bound) && bound <= (double)C) ? 1 : 0;
+  cert[h] = ok;
+  clis_head_stats_t st;
+  st.kappa = kappa;
+  st.qnorm_max = qmax;
+  st.bound = bound;
+  st.maxabs_v = vmax;
+  st.G = G;
+  st.L = L;
+  st.A = A;
+  st.C = C;
+  st.cert = ok;
+  st.reserved = 0;
+  stats[h] = st;
+}
+
 __global__ void __launch_bounds__(kThreads)
 cert_finalize(const double* __restrict__ vmax_part, const double* __restrict__ kap_part,
               const double* __restrict__ qss_part, int BH, int Nk, int Sk, int Sq, double c2,
               int32_t* __restrict__ cert, clis_head_stats_t* __restrict__ stats) {
-  for (int h = blockIdx.x * kThreads + threadIdx.x; h < BH; h += gridDim.x * kThreads) {
-    double vmax = 0.0, kap2 = 0.0, qss = 0.0;
-    for (int i = 0; i < Sk; ++i) {
-      vmax = max_keep_nan(vmax, vmax_part[(size_t)h * Sk + i]);
-      kap2 = max_keep_nan(kap2, kap_part[(size_t)h * Sk + i]);
-    }
-    for (int i = 0; i < Sq; ++i) qss = max_keep_nan(qss, qss_part[(size_t)h * Sq + i]);
-    const double kappa = sqrt(kap2);
-    const double qmax = sqrt(qss);
-    const double bound = (c2 * qmax) * kappa;
-    // step 5; a non-finite max |V| gets G = 128 so that C < 0
-    const int G = isfinite(vmax) ? ceil_log2_f64(vmax > 1.0 ? vmax : 1.0) : 128;
-    // step 6: ceil(log2 Nk) for Nk >= 1
-    const int L = (Nk <= 1) ? 0 : 32 - __clz(Nk - 1);
-    const int A = L + G;
-    // step 7 with the Figure 3 limits of fp32 accumulators and bf16/fp32 exp2
-    // outputs: log2 of the largest finite value is 127.99... in both formats,
-    // so floor(U_exp) = 127 and ceil(U_acc - A) - 1 = 127 - A for integer A.
-    const int C = min(127, 127 - A);
-    const int ok = (isfinite(bound) && bound <= (double)C) ? 1 : 0;
-    cert[h] = ok;
-    clis_head_stats_t st;
-    st.kappa = kappa;
-    st.qnorm_max = qmax;
-    st.bound = bound;
-    st.maxabs_v = vmax;
-    st.G = G;
-    st.L = L;
-    st.A = A;
-    st.C = C;
-    st.cert = ok;
-    st.reserved = 0;
-    stats[h] = st;
-  }
+  for (int h = blockIdx.x * kThreads + threadIdx.x; h < BH; h += gridDim.x * kThreads)
+    finalize_head(vmax_part, kap_part, qss_part, Nk, Sk, Sq, c2, cert, stats, h);
+}
+
+// Shapes with one key split and one query split: the four passes for one
+// head in one block, in the same order and with the same arithmetic as the
+// four kernels (so the results are bitwise theirs), one launch instead of
+// four.
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads)
+cert_small(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, int Nq, int Nk, double c2,
+           const float* __restrict__ vmax_blk, int nblk, double* __restrict__ ksum_part,
+           double* __restrict__ vmax_part, double* __restrict__ kbar, float* __restrict__ mu,
+           double* __restrict__ kap_part, double* __restrict__ qss_part, int32_t* __restrict__ cert,
+           clis_head_stats_t* __restrict__ stats) {
+  static_assert(D <= kThreads, "kbar: one thread per channel");
+  const int bh = blockIdx.x;
+  if (vmax_blk) keys_values_block<T, D, false>(K, V, Nk, 1, ksum_part, vmax_part, bh, 0);
+  else keys_values_block<T, D, true>(K, V, Nk, 1, ksum_part, vmax_part, bh, 0);
+  __syncthreads();  // the partial sums are in memory
+  kbar_block<D>(ksum_part, Nk, 1, kbar, vmax_blk, nblk, vmax_part, bh);
+  __syncthreads();  // kbar is in memory
+  norms_block<T, D>(Q, K, kbar, Nq, Nk, 1, 1, c2, mu, kap_part, qss_part, bh, 0);
+  norms_block<T, D>(Q, K, kbar, Nq, Nk, 1, 1, c2, mu, kap_part, qss_part, bh, 1);
+  __syncthreads();  // the partial maxima are in memory
+  if (threadIdx.x == 0) finalize_head(vmax_part, kap_part, qss_part, Nk, 1, 1, c2, cert, stats, bh);
 }
 
 __global__ void __launch_bounds__(64)
@@ -348,8 +408,16 @@ hipError_t certify_typed(const CertifyArgs& a, hipStream_t s) {
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
   if ((long long)BH * (Sk + Sq) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  cert_keys_values<T, D><<<(unsigned)(BH * Sk), kThreads, 0, s>>>(k, a.vmax_blk ? nullptr : v, a.Nk, Sk,
-                                                                   a.ksum_part, a.vmax_part);
+  if (Sk == 1 && Sq == 1) {
+    cert_small<T, D><<<(unsigned)BH, kThreads, 0, s>>>(q, k, v, a.Nq, a.Nk, c2, a.vmax_blk, a.vmax_nblk, a.ksum_part,
+                                                       a.vmax_part, a.kbar, a.mu, a.kap_part, a.qss_part, a.cert,
+                                                       a.stats);
+    return hipGetLastError();
+  }
+  if (a.vmax_blk)  // max |V| came with the V transpose
+    cert_keys_values<T, D, false><<<(unsigned)(BH * Sk), kThreads, 0, s>>>(k, v, a.Nk, Sk, a.ksum_part, a.vmax_part);
+  else
+    cert_keys_values<T, D, true><<<(unsigned)(BH * Sk), kThreads, 0, s>>>(k, v, a.Nk, Sk, a.ksum_part, a.vmax_part);
   cert_kbar<D><<<BH, D, 0, s>>>(a.ksum_part, a.Nk, Sk, a.kbar, a.vmax_blk, a.vmax_nblk, a.vmax_part);
   cert_norms<T, D><<<(unsigned)(BH * (Sk + Sq)), kThreads, 0, s>>>(q, k, a.kbar, a.Nq, a.Nk, Sk, Sq, c2, a.mu,
                                                                     a.kap_part, a.qss_part);
