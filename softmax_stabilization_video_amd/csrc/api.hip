@@ -230,6 +230,15 @@ int clis_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
     mu_use = mu_ws;
     cert_use = cert_ws;
   }
+  if (!needs_vt(dtype)) {  // fp32: one launch that routes each head itself
+    clis::AttnArgs f = a;
+    f.mu = mu_use;
+    f.route_out = route_out;
+    if (mode == CLIS_MODE_AUTO) f.cert = cert_use;
+    if ((e = launch_attn(f, dtype, mode == CLIS_MODE_FIXED, vt, s)) != hipSuccess)
+      return hip_fail(e, "attention launch");
+    return CLIS_OK;
+  }
   int32_t* lists = at<int32_t>(ws, L.lists);
   int32_t* counts = at<int32_t>(ws, L.counts);
   e = clis::launch_route(cert_use, mode, BH, lists, counts, route_out, s);

@@ -76,7 +76,8 @@ __device__ __forceinline__ void split_range(int n, int splits, int s, int* lo, i
   *hi = (int)b;
 }
 
-// Block-wide NaN-keeping max; every thread gets the result.
+// Block-wide NaN-keeping max over NTH threads; every thread gets the result.
+template <int NTH = kThreads>
 __device__ double block_max(double x, double* red) {
   for (int off = 32; off > 0; off >>= 1) x = max_keep_nan(x, __shfl_xor(x, off));
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -84,19 +85,19 @@ __device__ double block_max(double x, double* red) {
   if (lane == 0) red[wave] = x;
   __syncthreads();
   double r = red[0];
-  for (int i = 1; i < kThreads / 64; ++i) r = max_keep_nan(r, red[i]);
+  for (int i = 1; i < NTH / 64; ++i) r = max_keep_nan(r, red[i]);
   return r;
 }
 
 // Step 1 (partial column sums of K) and step 5 (partial max |V|).
-// (one block: head bh, key split `split`)
-template <typename T, int D, bool WITH_V>
+// (one block of NTH threads: head bh, key split `split`)
+template <typename T, int D, bool WITH_V, int NTH = kThreads>
 __device__ __forceinline__ void keys_values_block(const T* __restrict__ K, const T* __restrict__ V, int Nk, int Sk,
                                                   double* __restrict__ ksum_part, double* __restrict__ vmax_part,
                                                   int bh, int split) {
-  constexpr int VEC = Vec<T>::n, TPR = D / VEC, RPI = kThreads / TPR;
+  constexpr int VEC = Vec<T>::n, TPR = D / VEC, RPI = NTH / TPR;
   __shared__ double colsum[RPI][D];
-  __shared__ double red[kThreads / 64];
+  __shared__ double red[NTH / 64];
   int lo, hi;
   split_range(Nk, Sk, split, &lo, &hi);
   const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
@@ -136,9 +137,9 @@ __device__ __forceinline__ void keys_values_block(const T* __restrict__ K, const
   }
 #pragma unroll
   for (int e = 0; e < VEC; ++e) colsum[tr][tc * VEC + e] = acc[e];
-  vmax = block_max(vmax, red);  // contains __syncthreads
+  vmax = block_max<NTH>(vmax, red);  // contains __syncthreads
   double* out = ksum_part + ((size_t)bh * Sk + split) * D;
-  for (int c = threadIdx.x; c < D; c += kThreads) {
+  for (int c = threadIdx.x; c < D; c += NTH) {
     double s = 0.0;
     for (int r = 0; r < RPI; ++r) s += colsum[r][c];  // fixed row-group order
     out[c] = s;
@@ -296,18 +297,10 @@ __device__ __forceinline__ int ceil_log2_f64(double x) {
   return (f == 0.5) ? e - 1 : e;
 }
 
-// Steps 3-7 and the flag for head h (one thread).
-__device__ __forceinline__ void finalize_head(const double* __restrict__ vmax_part,
-                                              const double* __restrict__ kap_part,
-                                              const double* __restrict__ qss_part, int Nk, int Sk, int Sq,
-                                              double c2, int32_t* __restrict__ cert,
-                                              clis_head_stats_t* __restrict__ stats, int h) {
-  double vmax = 0.0, kap2 = 0.0, qss = 0.0;
-  for (int i = 0; i < Sk; ++i) {
-    vmax = max_keep_nan(vmax, vmax_part[(size_t)h * Sk + i]);
-    kap2 = max_keep_nan(kap2, kap_part[(size_t)h * Sk + i]);
-  }
-  for (int i = 0; i < Sq; ++i) qss = max_keep_nan(qss, qss_part[(size_t)h * Sq + i]);
+// Steps 3-7 and the flag for head h from its maxima (one thread).
+__device__ __forceinline__ void finalize_values(double vmax, double kap2, double qss, int Nk, double c2,
+                                                int32_t* __restrict__ cert, clis_head_stats_t* __restrict__ stats,
+                                                int h) {
   const double kappa = sqrt(kap2);
   const double qmax = sqrt(qss);
   const double bound = (c2 * qmax) * kappa;
@@ -336,6 +329,21 @@ __device__ __forceinline__ void finalize_head(const double* __restrict__ vmax_pa
   stats[h] = st;
 }
 
+// The same from the split partials, maxima taken in split order.
+__device__ __forceinline__ void finalize_head(const double* __restrict__ vmax_part,
+                                              const double* __restrict__ kap_part,
+                                              const double* __restrict__ qss_part, int Nk, int Sk, int Sq,
+                                              double c2, int32_t* __restrict__ cert,
+                                              clis_head_stats_t* __restrict__ stats, int h) {
+  double vmax = 0.0, kap2 = 0.0, qss = 0.0;
+  for (int i = 0; i < Sk; ++i) {
+    vmax = max_keep_nan(vmax, vmax_part[(size_t)h * Sk + i]);
+    kap2 = max_keep_nan(kap2, kap_part[(size_t)h * Sk + i]);
+  }
+  for (int i = 0; i < Sq; ++i) qss = max_keep_nan(qss, qss_part[(size_t)h * Sq + i]);
+  finalize_values(vmax, kap2, qss, Nk, c2, cert, stats, h);
+}
+
 __global__ void __launch_bounds__(kThreads)
 cert_finalize(const double* __restrict__ vmax_part, const double* __restrict__ kap_part,
               const double* __restrict__ qss_part, int BH, int Nk, int Sk, int Sq, double c2,
@@ -348,24 +356,95 @@ cert_finalize(const double* __restrict__ vmax_part, const double* __restrict__ k
 // head in one block, in the same order and with the same arithmetic as the
 // four kernels (so the results are bitwise theirs), one launch instead of
 // four.
-template <typename T, int D>
-__global__ void __launch_bounds__(kThreads)
+// Steps 2-3 for short sequences: the key norms and the query norms with the
+// stabilizers in one pass over the rows [K; Q] of head bh (the same per-row
+// arithmetic as norms_block); the two maxima go to *kap2 and *qss.
+template <typename T, int D, int NTH>
+__device__ __forceinline__ void norms_both_block(const T* __restrict__ Q, const T* __restrict__ K,
+                                                 const double* __restrict__ kbar, int Nq, int Nk, double c2,
+                                                 float* __restrict__ mu, int bh, double* kap2, double* qss) {
+  constexpr int VEC = Vec<T>::n, TPR = 8, RPI = NTH / TPR;
+  constexpr int NL = D / VEC / TPR;  // 16-byte loads per lane per row
+  constexpr int UN = NL > 2 ? kUnroll / 4 : kUnroll / 2;  // rows per lane in flight
+  static_assert(D % (VEC * TPR) == 0, "whole chunks per lane");
+  __shared__ double red[NTH / 64];
+  const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
+  double kb[NL][VEC];
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) kb[i][e] = kbar[(size_t)bh * D + (tc + TPR * i) * VEC + e];
+  const T* kbase = K + (size_t)bh * Nk * D;
+  const T* qbase = Q + (size_t)bh * Nq * D;
+  const int n = Nk + Nq;  // rows 0 .. Nk-1 are keys, the rest queries
+  double best_k = 0.0, best_q = 0.0;
+  // all lanes of a row group take the same row and trip count, so the DPP
+  // partners are always active
+  for (int j0 = 0; j0 < n; j0 += UN * RPI) {
+    uint4 ld[UN][NL];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int j = j0 + u * RPI + tr;
+      const T* row = j < Nk ? kbase + (size_t)j * D : qbase + (size_t)(j - Nk) * D;
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        ld[u][i] = j < n ? *reinterpret_cast<const uint4*>(row + (tc + TPR * i) * VEC) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int j = j0 + u * RPI + tr;
+      const bool key = j < Nk;
+      double ss = 0.0, dot = 0.0;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        double x[VEC];
+        widen<T>(ld[u][i], x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          if (key) {
+            const double t = x[e] - kb[i][e];
+            ss += t * t;
+          } else {
+            ss += x[e] * x[e];
+            dot += x[e] * kb[i][e];
+          }
+        }
+      }
+      ss = row8_sum(ss);
+      dot = row8_sum(dot);
+      if (key) {
+        best_k = max_keep_nan(best_k, ss);
+      } else if (j < n) {
+        best_q = max_keep_nan(best_q, ss);
+        if (tc == 0) mu[(size_t)bh * Nq + (j - Nk)] = (float)(c2 * dot);
+      }
+    }
+  }
+  *kap2 = block_max<NTH>(best_k, red);
+  *qss = block_max<NTH>(best_q, red);
+}
+
+// Certification of one head per block of kSmallThreads threads, for one key
+// split and one query split: column sums, kbar, the norm pass over keys and
+// queries together, and the flag -- one launch instead of four.
+constexpr int kSmallThreads = 1024;
+
+template <typename T, int D, bool WITH_V>
+__global__ void __launch_bounds__(kSmallThreads)
 cert_small(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, int Nq, int Nk, double c2,
            const float* __restrict__ vmax_blk, int nblk, double* __restrict__ ksum_part,
            double* __restrict__ vmax_part, double* __restrict__ kbar, float* __restrict__ mu,
-           double* __restrict__ kap_part, double* __restrict__ qss_part, int32_t* __restrict__ cert,
-           clis_head_stats_t* __restrict__ stats) {
-  static_assert(D <= kThreads, "kbar: one thread per channel");
+           int32_t* __restrict__ cert, clis_head_stats_t* __restrict__ stats) {
+  static_assert(D <= kSmallThreads, "kbar: one thread per channel");
   const int bh = blockIdx.x;
-  if (vmax_blk) keys_values_block<T, D, false>(K, V, Nk, 1, ksum_part, vmax_part, bh, 0);
-  else keys_values_block<T, D, true>(K, V, Nk, 1, ksum_part, vmax_part, bh, 0);
-  __syncthreads();  // the partial sums are in memory
+  keys_values_block<T, D, WITH_V, kSmallThreads>(K, V, Nk, 1, ksum_part, vmax_part, bh, 0);
+  __syncthreads();  // the column sums are in memory
   kbar_block<D>(ksum_part, Nk, 1, kbar, vmax_blk, nblk, vmax_part, bh);
   __syncthreads();  // kbar is in memory
-  norms_block<T, D>(Q, K, kbar, Nq, Nk, 1, 1, c2, mu, kap_part, qss_part, bh, 0);
-  norms_block<T, D>(Q, K, kbar, Nq, Nk, 1, 1, c2, mu, kap_part, qss_part, bh, 1);
-  __syncthreads();  // the partial maxima are in memory
-  if (threadIdx.x == 0) finalize_head(vmax_part, kap_part, qss_part, Nk, 1, 1, c2, cert, stats, bh);
+  double kap2, qss;
+  norms_both_block<T, D, kSmallThreads>(Q, K, kbar, Nq, Nk, c2, mu, bh, &kap2, &qss);
+  // thread 0 wrote vmax_part[bh] itself (in either pass above)
+  if (threadIdx.x == 0) finalize_values(vmax_part[bh], kap2, qss, Nk, c2, cert, stats, bh);
 }
 
 __global__ void __launch_bounds__(64)
@@ -409,9 +488,10 @@ hipError_t certify_typed(const CertifyArgs& a, hipStream_t s) {
   const T* v = static_cast<const T*>(a.v);
   if ((long long)BH * (Sk + Sq) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (Sk == 1 && Sq == 1) {
-    cert_small<T, D><<<(unsigned)BH, kThreads, 0, s>>>(q, k, v, a.Nq, a.Nk, c2, a.vmax_blk, a.vmax_nblk, a.ksum_part,
-                                                       a.vmax_part, a.kbar, a.mu, a.kap_part, a.qss_part, a.cert,
-                                                       a.stats);
+    // without V when max |V| came with the V transpose
+    auto kern = a.vmax_blk ? cert_small<T, D, false> : cert_small<T, D, true>;
+    kern<<<(unsigned)BH, kSmallThreads, 0, s>>>(q, k, v, a.Nq, a.Nk, c2, a.vmax_blk, a.vmax_nblk, a.ksum_part,
+                                                a.vmax_part, a.kbar, a.mu, a.cert, a.stats);
     return hipGetLastError();
   }
   if (a.vmax_blk)  // max |V| came with the V transpose

@@ -130,6 +130,11 @@ struct AttnArgs {
   float* tail_l = nullptr;    // [kTailSlots][kTailRows]
   int* sched = nullptr;       // pool counter, zero at launch, or NULL: no pool
   const int32_t* split_heads = nullptr;  // device count of listed heads < kSplitHeads
+  // fp32 kernel only (it takes no head list): if cert is set, each head runs
+  // fixed when cert[head] != 0 and online otherwise (auto mode); route_out
+  // (or NULL) receives 1 for a fixed head, 0 for an online one.
+  const int32_t* cert = nullptr;
+  int32_t* route_out = nullptr;
 };
 
 // bf16 kernels: V is read through a transposed copy [BH][vt_pad(Nk) / 64]
@@ -138,6 +143,8 @@ struct AttnArgs {
 hipError_t launch_transpose_v(const void* v, void* vt, int BH, int Nk, int d, hipStream_t s,
                               float* vmax_blk = nullptr);
 hipError_t launch_attn_bf16(const AttnArgs& a, bool fixed, const void* vt, hipStream_t s);
+// fp32 kernel: every head of the grid (no head list); routes as AttnArgs::cert
+// says, else fixed or online as `fixed` says.
 hipError_t launch_attn_fp32(const AttnArgs& a, bool fixed, hipStream_t s);
 
 // O = o_acc / l (bf16 or fp32), and lse = ln 2 (mu + log2 l) if lse is set.
