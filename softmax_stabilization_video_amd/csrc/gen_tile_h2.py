@@ -64,6 +64,7 @@ NF = 3                     # fragment ring slots
 FB = SB + 32               # first fragment register
 T0 = FB + 4 * NF           # address temporaries
 PRIO = 3                   # wave priority while issuing MFMAs
+ANCHOR_NOPS = 1            # no-ops after the block's 256-byte boundary
 HZ_MFMA_VALU = 12
 HZ_VALU_MFMA = 5
 HZ_TRANS = 2
@@ -177,6 +178,7 @@ def generate(parts, tag):
     scores / packed weights of the part in flight.  `tag` keeps labels apart."""
     ks, vs, vsp, mf, mfp, lim = "ks", "vs", "vsp", "mf", "mfp", "lim"
     g = Gen()
+    last_phase = [None]
     loads = load_items(tag)
     n_mfma = sum(16 for p in parts if not p.startswith("sm"))
     every = max(1, n_mfma // (len(loads) + 1))
@@ -273,6 +275,13 @@ def generate(parts, tag):
         # wave priority: high while issuing products, low during the weights,
         # so the other wave on the SIMD gets its products issued meanwhile
         g.emit(f"s_setprio {0 if p.startswith('sm') else PRIO}")
+        # in the two main variants a weights phase starts once the fragment
+        # reads already issued for the next products have landed (measured
+        # faster together with the block's placement, see main())
+        phase = "V" if p.startswith("sm") else "M"
+        if tag in ("amain", "bmain") and last_phase[0] == "M" and phase == "V":
+            g.emit("s_waitcnt lgkmcnt(0)")
+        last_phase[0] = phase
         if p.startswith("qk"):
             # scores: the two halves' chains alternate, each K fragment feeds both
             for st in range(NS):
@@ -357,7 +366,14 @@ def main():
     here = os.path.dirname(os.path.abspath(__file__))
     text = ["// tile_h2.inc -- generated by gen_tile_h2.py; do not edit.",
             "// Fixed-stabilizer tile window, two 32-row query halves per wave, d = 128."]
-    lines = []
+    # Placement.  The block's performance depends on where its instructions
+    # sit relative to 256-byte boundaries (layouts that differ by a few
+    # no-ops measured up to 7% apart), so it starts at a fixed offset from
+    # one: a jump over padding to a 256-byte boundary, then ANCHOR_NOPS
+    # no-ops (the best of the offsets measured), and its end is padded to a
+    # 64-byte boundary, so the code around it does not move it and it does
+    # not move the code after it by less than that.
+    lines = ["s_branch .Lanchor_%=", ".p2align 8", ".Lanchor_%=:"] + ["s_nop 0"] * ANCHOR_NOPS
     for i, (tag, _) in enumerate(VARIANTS[1:], 1):
         lines += [f"s_cmp_eq_u32 %[kind], {i}", f"s_cbranch_scc1 .Lv{tag}_%="]
     for i, (tag, parts) in enumerate(VARIANTS):
@@ -371,7 +387,8 @@ def main():
             lines.append(f".Lv{tag}_%=:")
         lines += body
         lines.append("s_branch .Lend_%=")
-    lines[-1] = ".Lend_%=:"
+    lines[-1] = ".p2align 6"
+    lines.append(".Lend_%=:")
     body = " \\\n".join(f'  "{l}\\n"' for l in lines)
     text.append(f"#define CLIS_TILE_H2_WINDOW \\\n{body}")
     text.append("#define CLIS_TILE_H2_CLOBBERS \\")
