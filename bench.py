@@ -39,11 +39,12 @@ CSRC = os.path.join(ROOT, "softmax_stabilization_video_amd", "csrc")
 
 
 def dominant_kernel(w):
-    """(name, source) of the fixed-stabilizer kernel that runs this workload."""
+    """(name, source files) of the fixed-stabilizer kernel that runs this workload."""
     c = "true" if w.causal else "false"
     if w.dtype == "bf16":
         h = 2 if w.d == 128 else 1  # row halves per wave of the fixed kernel that returns O
-        return f"attn_fwd_bf16<{w.d}, true, {c}, 8, false, false, {h}>", os.path.join(CSRC, "attn_bf16.hip")
+        return (f"attn_fwd_bf16<{w.d}, true, {c}, 8, false, false, {h}>",
+                (os.path.join(CSRC, "attn_bf16.hip"), os.path.join(CSRC, "tile_h2.inc")))
     # fp32: the kernel instance with every head on the fixed route (route 1)
     return f"attn_fwd_fp32<{w.d}, 1, {c}, false>", os.path.join(CSRC, "attn_fp32.hip")
 
@@ -52,8 +53,12 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    """First 16 hex digits of the sha256 of the kernel's source files, in order."""
+    h = hashlib.sha256()
+    for path in ([paths] if isinstance(paths, str) else paths):
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def time_calls(fn, n: int, stream) -> list:
