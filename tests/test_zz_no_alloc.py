@@ -23,20 +23,21 @@ def clis():
 
 
 CASES = [
-    # name, B, H, N, d, causal, seed
-    ("larger", 2, 5, 2000, 128, False, 21),
-    ("smaller", 1, 3, 700, 64, False, 22),
-    ("smaller_causal", 1, 2, 500, 128, True, 23),
+    # name, B, H, N, d, causal, seed, dtype
+    ("larger", 2, 5, 2000, 128, False, 21, "bf16"),
+    ("smaller", 1, 3, 700, 64, False, 22, "bf16"),
+    ("smaller_causal", 1, 2, 500, 128, True, 23, "bf16"),
+    ("fp32", 1, 4, 600, 64, False, 24, "fp32"),
 ]
 
 
-def _run_case(clis, name, B, H, N, d, causal, seed, mode):
+def _run_case(clis, name, B, H, N, d, causal, seed, dtype, mode):
     import torch
-    w = workloads.custom(f"noalloc_{name}", B, H, N, d, "bf16", causal, base="mixed", fail_frac=0.4)
+    w = workloads.custom(f"noalloc_{name}", B, H, N, d, dtype, causal, base="mixed", fail_frac=0.4)
     assert clis.workspace_bytes(B, H, N, N, d) <= clis.NOALLOC_SCRATCH_BYTES
     Q, K, V = workloads.make_inputs(w, seed)
-    q, k, v = (to_device(a, "bf16") for a in (Q, K, V))
-    say("noalloc", name, mode, B, H, N, d, "causal" if causal else "dense")
+    q, k, v = (to_device(a, dtype) for a in (Q, K, V))
+    say("noalloc", name, mode, B, H, N, d, dtype, "causal" if causal else "dense")
     ref, ref_route, ref_lse = clis.clis_attn_fwd(q, k, v, w.scale, causal, mode=mode, want_route=True,
                                                  want_lse=True)
     o = torch.full_like(q, float("nan"))
