@@ -40,11 +40,6 @@ template <typename T> struct Vec;
 template <> struct Vec<uint16_t> { static constexpr int n = 8; };
 template <> struct Vec<float> { static constexpr int n = 4; };
 
-__device__ __forceinline__ double to_f64(uint16_t b) {
-  return (double)__uint_as_float((uint32_t)b << 16);
-}
-__device__ __forceinline__ double to_f64(float f) { return (double)f; }
-
 // Rows in flight per lane in the streaming loops (loads issued before use):
 // enough that a CU keeps 64 KB or more of reads outstanding.
 constexpr int kUnroll = 8;
@@ -93,8 +88,7 @@ __device__ double block_max(double x, double* red) {
 // (one block of NTH threads: head bh, key split `split`)
 template <typename T, int D, bool WITH_V, int NTH = kThreads>
 __device__ __forceinline__ void keys_values_block(const T* __restrict__ K, const T* __restrict__ V, int Nk, int Sk,
-                                                  double* __restrict__ ksum_part, double* __restrict__ vmax_part,
-                                                  int bh, int split) {
+                                                  double* out, double* vmax_out, int bh, int split) {
   constexpr int VEC = Vec<T>::n, TPR = D / VEC, RPI = NTH / TPR;
   __shared__ double colsum[RPI][D];
   __shared__ double red[NTH / 64];
@@ -138,13 +132,12 @@ __device__ __forceinline__ void keys_values_block(const T* __restrict__ K, const
 #pragma unroll
   for (int e = 0; e < VEC; ++e) colsum[tr][tc * VEC + e] = acc[e];
   vmax = block_max<NTH>(vmax, red);  // contains __syncthreads
-  double* out = ksum_part + ((size_t)bh * Sk + split) * D;
   for (int c = threadIdx.x; c < D; c += NTH) {
     double s = 0.0;
     for (int r = 0; r < RPI; ++r) s += colsum[r][c];  // fixed row-group order
     out[c] = s;
   }
-  if (threadIdx.x == 0) vmax_part[(size_t)bh * Sk + split] = vmax;
+  if (threadIdx.x == 0) *vmax_out = vmax;
 }
 
 template <typename T, int D, bool WITH_V>
@@ -152,36 +145,49 @@ __global__ void __launch_bounds__(kThreads)
 cert_keys_values(const T* __restrict__ K, const T* __restrict__ V, int Nk, int Sk,
                  double* __restrict__ ksum_part, double* __restrict__ vmax_part) {
   // 1-D grid: any head count
-  keys_values_block<T, D, WITH_V>(K, V, Nk, Sk, ksum_part, vmax_part, blockIdx.x / Sk, blockIdx.x % Sk);
+  keys_values_block<T, D, WITH_V>(K, V, Nk, Sk, ksum_part + (size_t)blockIdx.x * D, vmax_part + blockIdx.x,
+                                  blockIdx.x / Sk, blockIdx.x % Sk);
 }
 
 // Step 1: kbar from the split partials, summed in split order (threads c <
-// D of the block; every thread reaches the barrier).
+// D of the block; every thread reaches the barrier).  The head's partial sums
+// `sums` ([Sk][D]) -> kbar ([D], and kbar_copy if set); with vmax_blk (the
+// head's nblk block maxima of |V|) their maximum goes to *vmax_out (split 0's
+// partial).
 template <int D>
-__device__ __forceinline__ void kbar_block(const double* __restrict__ ksum_part, int Nk, int Sk,
-                                           double* __restrict__ kbar, const float* __restrict__ vmax_blk, int nblk,
-                                           double* __restrict__ vmax_part, int bh) {
+__device__ __forceinline__ void kbar_block_impl(const double* sums, int Nk, int Sk, double* __restrict__ kbar,
+                                                double* kbar_copy, const float* __restrict__ vmax_blk, int nblk,
+                                                double* vmax_out, double* red) {
   const int c = threadIdx.x;
-  if (vmax_blk) {  // block maxima of |V| from the transpose -> split 0's partial
-    __shared__ double red[(D + 63) / 64];
+  if (vmax_blk) {
     double m = 0.0;
     if (c < D)
-      for (int i = c; i < nblk; i += D) m = max_keep_nan(m, (double)vmax_blk[(size_t)bh * nblk + i]);
+      for (int i = c; i < nblk; i += D) m = max_keep_nan(m, (double)vmax_blk[i]);
     for (int off = 32; off > 0; off >>= 1) m = max_keep_nan(m, __shfl_xor(m, off));
     if (c < D && (c & 63) == 0) red[c >> 6] = m;
     __syncthreads();
     if (c == 0) {
       double r = red[0];
       for (int w = 1; w < (D + 63) / 64; ++w) r = max_keep_nan(r, red[w]);
-      vmax_part[(size_t)bh * Sk] = r;
+      *vmax_out = r;
     }
   }
   if (c < D) {
-    const double* p = ksum_part + (size_t)bh * Sk * D + c;
+    const double* p = sums + c;
     double s = 0.0;
     for (int i = 0; i < Sk; ++i) s += p[(size_t)i * D];
-    kbar[(size_t)bh * D + c] = s / (double)Nk;
+    kbar[c] = s / (double)Nk;
+    if (kbar_copy) kbar_copy[c] = s / (double)Nk;
   }
+}
+
+template <int D>
+__device__ __forceinline__ void kbar_block(const double* __restrict__ ksum_part, int Nk, int Sk,
+                                           double* __restrict__ kbar, const float* __restrict__ vmax_blk, int nblk,
+                                           double* __restrict__ vmax_part, int bh) {
+  __shared__ double red[(D + 63) / 64];
+  kbar_block_impl<D>(ksum_part + (size_t)bh * Sk * D, Nk, Sk, kbar + (size_t)bh * D, nullptr,
+                     vmax_blk ? vmax_blk + (size_t)bh * nblk : nullptr, nblk, vmax_part + (size_t)bh * Sk, red);
 }
 
 template <int D>
@@ -361,7 +367,7 @@ cert_finalize(const double* __restrict__ vmax_part, const double* __restrict__ k
 // arithmetic as norms_block); the two maxima go to *kap2 and *qss.
 template <typename T, int D, int NTH>
 __device__ __forceinline__ void norms_both_block(const T* __restrict__ Q, const T* __restrict__ K,
-                                                 const double* __restrict__ kbar, int Nq, int Nk, double c2,
+                                                 const double* kbar_head, int Nq, int Nk, double c2,
                                                  float* __restrict__ mu, int bh, double* kap2, double* qss) {
   constexpr int VEC = Vec<T>::n, TPR = 8, RPI = NTH / TPR;
   constexpr int NL = D / VEC / TPR;  // 16-byte loads per lane per row
@@ -373,7 +379,7 @@ __device__ __forceinline__ void norms_both_block(const T* __restrict__ Q, const 
 #pragma unroll
   for (int i = 0; i < NL; ++i)
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) kb[i][e] = kbar[(size_t)bh * D + (tc + TPR * i) * VEC + e];
+    for (int e = 0; e < VEC; ++e) kb[i][e] = kbar_head[(tc + TPR * i) * VEC + e];
   const T* kbase = K + (size_t)bh * Nk * D;
   const T* qbase = Q + (size_t)bh * Nq * D;
   const int n = Nk + Nq;  // rows 0 .. Nk-1 are keys, the rest queries
@@ -432,19 +438,20 @@ constexpr int kSmallThreads = 1024;
 template <typename T, int D, bool WITH_V>
 __global__ void __launch_bounds__(kSmallThreads)
 cert_small(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, int Nq, int Nk, double c2,
-           const float* __restrict__ vmax_blk, int nblk, double* __restrict__ ksum_part,
-           double* __restrict__ vmax_part, double* __restrict__ kbar, float* __restrict__ mu,
+           const float* __restrict__ vmax_blk, int nblk, double* __restrict__ kbar, float* __restrict__ mu,
            int32_t* __restrict__ cert, clis_head_stats_t* __restrict__ stats) {
   static_assert(D <= kSmallThreads, "kbar: one thread per channel");
+  // the head's column sums, kbar and max |V| stay in LDS between the passes
+  __shared__ double sums[D], kb[D], red[(D + 63) / 64], vmax;
   const int bh = blockIdx.x;
-  keys_values_block<T, D, WITH_V, kSmallThreads>(K, V, Nk, 1, ksum_part, vmax_part, bh, 0);
-  __syncthreads();  // the column sums are in memory
-  kbar_block<D>(ksum_part, Nk, 1, kbar, vmax_blk, nblk, vmax_part, bh);
-  __syncthreads();  // kbar is in memory
+  keys_values_block<T, D, WITH_V, kSmallThreads>(K, V, Nk, 1, sums, &vmax, bh, 0);
+  __syncthreads();  // the column sums are in LDS
+  kbar_block_impl<D>(sums, Nk, 1, kbar + (size_t)bh * D, kb, vmax_blk ? vmax_blk + (size_t)bh * nblk : nullptr,
+                     nblk, &vmax, red);
+  __syncthreads();  // kbar (and max |V|) are in LDS
   double kap2, qss;
-  norms_both_block<T, D, kSmallThreads>(Q, K, kbar, Nq, Nk, c2, mu, bh, &kap2, &qss);
-  // thread 0 wrote vmax_part[bh] itself (in either pass above)
-  if (threadIdx.x == 0) finalize_values(vmax_part[bh], kap2, qss, Nk, c2, cert, stats, bh);
+  norms_both_block<T, D, kSmallThreads>(Q, K, kb, Nq, Nk, c2, mu, bh, &kap2, &qss);
+  if (threadIdx.x == 0) finalize_values(vmax, kap2, qss, Nk, c2, cert, stats, bh);
 }
 
 __global__ void __launch_bounds__(64)
@@ -490,8 +497,8 @@ hipError_t certify_typed(const CertifyArgs& a, hipStream_t s) {
   if (Sk == 1 && Sq == 1) {
     // without V when max |V| came with the V transpose
     auto kern = a.vmax_blk ? cert_small<T, D, false> : cert_small<T, D, true>;
-    kern<<<(unsigned)BH, kSmallThreads, 0, s>>>(q, k, v, a.Nq, a.Nk, c2, a.vmax_blk, a.vmax_nblk, a.ksum_part,
-                                                a.vmax_part, a.kbar, a.mu, a.cert, a.stats);
+    kern<<<(unsigned)BH, kSmallThreads, 0, s>>>(q, k, v, a.Nq, a.Nk, c2, a.vmax_blk, a.vmax_nblk, a.kbar, a.mu,
+                                                a.cert, a.stats);
     return hipGetLastError();
   }
   if (a.vmax_blk)  // max |V| came with the V transpose
