@@ -144,8 +144,9 @@ attn_fwd_fp32(const float* __restrict__ Q, const float* __restrict__ K, const fl
   if (wave < n_kt) load_tile<D>(cur, Kh, Vh, wave * kTile, Nk, h, col);
   for (int it = wave; it < n_kt; it += kWaves) {
     const int kt = it * kTile;
+    // the next tile (the wave's last tile loads itself again, unused)
     TileRegs<D> nxt;
-    if (it + kWaves < n_kt) load_tile<D>(nxt, Kh, Vh, kt + kWaves * kTile, Nk, h, col);
+    load_tile<D>(nxt, Kh, Vh, it + kWaves < n_kt ? kt + kWaves * kTile : kt, Nk, h, col);
 
     floatx16 s;
 #pragma unroll
