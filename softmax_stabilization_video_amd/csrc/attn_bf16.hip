@@ -23,8 +23,8 @@
 // Table 7 caption).
 //
 // Work decomposition.  A workgroup of WAVES waves owns 32*H*WAVES query rows
-// of one (batch, head); each wave owns H 32-row halves (H = 1, or H = 2 in the
-// fixed form that returns O at d = 128), and two waves share a SIMD.  K and
+// of one (batch, head); each wave owns H 32-row halves (H = 2 in the fixed
+// forms at d = 128, H = 1 otherwise), and two waves share a SIMD.  K and
 // V^T tiles of 64 keys stream through an LDS ring, loaded with buffer loads
 // that write LDS directly (buffer_load_dword[x4] ... lds), one barrier per
 // tile.  Both products use v_mfma_f32_32x32x16_bf16 with fp32 accumulation,
@@ -294,7 +294,7 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               int* __restrict__ sched, const int32_t* __restrict__ split_heads) {
   static_assert(FIXED || !PARTIAL, "key shards use the fixed stabilizer");
   static_assert(!(FIXED && LAZY), "lazy rescaling is an online-softmax form");
-  static_assert(H == 1 || (H == 2 && FIXED && !PARTIAL), "two row halves per wave: fixed path, output O");
+  static_assert(H == 1 || (H == 2 && FIXED), "two row halves per wave: fixed path");
   using G = Geo<D, WAVES, H>;
   constexpr bool PAD = H == 2;  // padded LDS tile rows (else swizzled)
   const int kv_offset = PARTIAL ? kv_offset_arg : 0;  // global index of key 0
@@ -468,19 +468,23 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[h][c][r] = 0.f;
   }
-  if (PARTIAL && accumulate && qvalid[0]) {  // continue the sums of earlier key shards
-    const float* arow = o_acc + qoff[0];
+  if (PARTIAL && accumulate) {  // continue the sums of earlier key shards
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int h = 0; h < H; ++h) {
+      if (!qvalid[h]) continue;
+      const float* arow = o_acc + qoff[h];
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const float4 t = *reinterpret_cast<const float4*>(arow + c * 32 + 8 * rq + 4 * g);
-        oacc[0][c][4 * rq + 0] = t.x;
-        oacc[0][c][4 * rq + 1] = t.y;
-        oacc[0][c][4 * rq + 2] = t.z;
-        oacc[0][c][4 * rq + 3] = t.w;
-      }
-    if (g == 0) lsum[0] = l_acc[(size_t)bh * Nq + qrow[0]];
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const float4 t = *reinterpret_cast<const float4*>(arow + c * 32 + 8 * rq + 4 * g);
+          oacc[h][c][4 * rq + 0] = t.x;
+          oacc[h][c][4 * rq + 1] = t.y;
+          oacc[h][c][4 * rq + 2] = t.z;
+          oacc[h][c][4 * rq + 3] = t.w;
+        }
+      if (g == 0) lsum[h] = l_acc[(size_t)bh * Nq + qrow[h]];
+    }
   }
 
 
@@ -759,15 +763,17 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     return;
   }
   if constexpr (PARTIAL) {  // key shard: the unnormalized sums
-    if (qvalid[0]) {
-      float* arow = o_acc + qoff[0];
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      if (!qvalid[h]) continue;
+      float* arow = o_acc + qoff[h];
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq)
           *reinterpret_cast<float4*>(arow + c * 32 + 8 * rq + 4 * g) = make_float4(
-              oacc[0][c][4 * rq], oacc[0][c][4 * rq + 1], oacc[0][c][4 * rq + 2], oacc[0][c][4 * rq + 3]);
-      if (g == 0) l_acc[(size_t)bh * Nq + qrow[0]] = lsum[0];
+              oacc[h][c][4 * rq], oacc[h][c][4 * rq + 1], oacc[h][c][4 * rq + 2], oacc[h][c][4 * rq + 3]);
+      if (g == 0) l_acc[(size_t)bh * Nq + qrow[h]] = lsum[h];
     }
     return;
   }
@@ -845,7 +851,7 @@ int cu_count() {
 template <int D, bool FIXED, bool CAUSAL, bool PARTIAL = false, bool LAZY = false>
 hipError_t launch_t(const AttnArgs& a, const uint16_t* vt, int nk_pad, hipStream_t s) {
   constexpr int WAVES = FIXED ? (CAUSAL ? CLIS_FIXED_CAUSAL_WAVES : CLIS_FIXED_WAVES) : CLIS_ONLINE_WAVES;
-  constexpr int H = (FIXED && !PARTIAL && D == 128) ? (CAUSAL ? CLIS_FIXED_CAUSAL_HALVES : CLIS_FIXED_HALVES) : 1;
+  constexpr int H = (FIXED && D == 128) ? (CAUSAL ? CLIS_FIXED_CAUSAL_HALVES : CLIS_FIXED_HALVES) : 1;
   using G = Geo<D, WAVES, H>;
   const int n_qt = (a.Nq + G::BM - 1) / G::BM;
   // pooled work of the dense forms (file comment): conc workgroups are
