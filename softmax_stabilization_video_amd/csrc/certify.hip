@@ -40,6 +40,14 @@ template <typename T> struct Vec;
 template <> struct Vec<uint16_t> { static constexpr int n = 8; };
 template <> struct Vec<float> { static constexpr int n = 4; };
 
+// 16 bytes of a row that this pass reads once: a nontemporal load (the
+// streaming hint keeps the single-use rows from displacing cached data;
+// measured 7-9% faster certification on the long workloads).
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load16(const void* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(static_cast<const u32x4v*>(p)));
+}
+
 // Rows in flight per lane in the streaming loops (loads issued before use):
 // enough that a CU keeps 64 KB or more of reads outstanding.
 constexpr int kUnroll = 8;
@@ -111,8 +119,8 @@ __device__ __forceinline__ void keys_values_block(const T* __restrict__ K, const
       uk[u] = make_uint4(0, 0, 0, 0);
       if constexpr (WITH_V) uv[u] = make_uint4(0, 0, 0, 0);
       if (j < hi) {
-        uk[u] = *reinterpret_cast<const uint4*>(kb + (size_t)j * D + tc * VEC);
-        if constexpr (WITH_V) uv[u] = *reinterpret_cast<const uint4*>(vb + (size_t)j * D + tc * VEC);
+        uk[u] = stream_load16(kb + (size_t)j * D + tc * VEC);
+        if constexpr (WITH_V) uv[u] = stream_load16(vb + (size_t)j * D + tc * VEC);
       }
     }
 #pragma unroll
@@ -252,7 +260,7 @@ __device__ __forceinline__ void norms_block(const T* __restrict__ Q, const T* __
       const int j = j0 + u * RPI + tr;
 #pragma unroll
       for (int i = 0; i < NL; ++i)
-        ld[u][i] = j < hi ? *reinterpret_cast<const uint4*>(base + (size_t)j * D + (tc + TPR * i) * VEC)
+        ld[u][i] = j < hi ? stream_load16(base + (size_t)j * D + (tc + TPR * i) * VEC)
                           : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
@@ -394,7 +402,7 @@ __device__ __forceinline__ void norms_both_block(const T* __restrict__ Q, const 
       const T* row = j < Nk ? kbase + (size_t)j * D : qbase + (size_t)(j - Nk) * D;
 #pragma unroll
       for (int i = 0; i < NL; ++i)
-        ld[u][i] = j < n ? *reinterpret_cast<const uint4*>(row + (tc + TPR * i) * VEC) : make_uint4(0, 0, 0, 0);
+        ld[u][i] = j < n ? stream_load16(row + (tc + TPR * i) * VEC) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < UN; ++u) {

@@ -15,6 +15,8 @@
 namespace clis {
 namespace {
 
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
 constexpr int kTK = 64;  // keys per block (also the max |V| block)
 
 // Position of key k within its 16-key group in V^T: swap bits 2 and 3.
@@ -39,7 +41,8 @@ transpose_v(const uint16_t* __restrict__ V, uint16_t* __restrict__ Vt, int Nk, i
   for (int i = threadIdx.x; i < kTK * CPR; i += 256) {
     const int r = i / CPR, ch = i % CPR, key = kt + r;
     uint4 u = make_uint4(0, 0, 0, 0);
-    if (key < Nk) u = *reinterpret_cast<const uint4*>(src + (size_t)key * D + ch * 8);
+    if (key < Nk)  // V is read once here: a nontemporal (streaming) load
+      u = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(src + (size_t)key * D + ch * 8)));
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
     if (vmax_blk) {
 #pragma unroll
