@@ -85,3 +85,19 @@ def test_generated_code_uses_only_listed_instructions():
                 or o in allowed_scalar), o
     assert not any(o.startswith("v_pk_") for o in ops)
     assert {o for o in ops if "mfma" in o} == {"v_mfma_f32_32x32x16_bf16"}
+
+
+def test_block_placement():
+    """The block starts with a jump over padding to a 256-byte boundary (plus
+    the chosen no-ops) and ends on a 64-byte boundary, so the code around it
+    does not move it (its speed depends on its placement)."""
+    text = open(os.path.join(CSRC, "tile_h2.inc")).read()
+    lines = re.findall(r'^\s*"([^"]*)\\n"', text, re.M)
+    g = _gen()
+    assert lines[:3] == ["s_branch .Lanchor_%=", ".p2align 8", ".Lanchor_%=:"]
+    assert lines[3:3 + g.ANCHOR_NOPS] == ["s_nop 0"] * g.ANCHOR_NOPS
+    assert not lines[3 + g.ANCHOR_NOPS].startswith("s_nop")
+    assert lines[-2:] == [".p2align 6", ".Lend_%=:"]
+    # every variant is left by a jump to the end except the last, which falls
+    # into the padding and the end label
+    assert sum(1 for l in lines if l == "s_branch .Lend_%=") == len(g.VARIANTS) - 1
