@@ -235,7 +235,7 @@ __device__ __forceinline__ void norms_block(const T* __restrict__ Q, const T* __
                                             double* __restrict__ qss_part, int bh, int part) {
   constexpr int VEC = Vec<T>::n, TPR = 8, RPI = kThreads / TPR;
   constexpr int NL = D / VEC / TPR;  // 16-byte loads per lane per row
-  constexpr int UN = NL > 2 ? kUnroll / 2 : kUnroll;  // rows per lane in flight
+  constexpr int UN = kUnroll / 2;  // rows per lane in flight (more measured slower: registers)
   static_assert(D % (VEC * TPR) == 0, "whole chunks per lane");
   __shared__ double red[kThreads / 64];
   const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
