@@ -441,7 +441,7 @@ def test_max_keys_uniform_weights(clis):
 
 
 # ---------------------------------------------------------------- many heads
-@pytest.mark.parametrize("dtype,d,fail_scale", [("bf16", 64, 4.0), ("fp32", 128, 1.0)])
+@pytest.mark.parametrize("dtype,d,fail_scale", [("bf16", 64, 4.0), ("bf16", 128, 4.0), ("fp32", 128, 1.0)])
 def test_many_heads_beyond_a_grid_dimension(clis, dtype, d, fail_scale):
     """66,000 (batch, head) pairs, more than a launch grid's second dimension
     holds: certification, the V transpose and attention index heads along
