@@ -144,11 +144,13 @@ int clis_certify(const void* q, const void* k, const void* v,
  *              row sum l_i, the online path as ln 2 * (m_i + log2 l_i) from its
  *              final running maximum; no extra pass over the keys.
  *   ws         device workspace (clis_workspace_bytes()); may be NULL only if
- *              mode is online and dtype is fp32.
+ *              mode is online or online_lazy, dtype is fp32 and route_out is
+ *              NULL.
  * Output dtype equals input dtype: fp32 accumulation, bf16 stored with round
  * to nearest even; on the bf16 path the exp2 weights are rounded to bf16
- * (nearest even) before the P.V product, and the row sums (hence lse) add the
- * same rounded weights.
+ * (nearest even) before the P.V product; the row sums (hence lse) add the
+ * fp32 weights on the fixed path and the rounded weights on the online path.
+ * fp32 inputs run one kernel that takes each head's route from cert itself.
  */
 int clis_attn_fwd(const void* q, const void* k, const void* v, void* o,
                   int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
