@@ -12,8 +12,9 @@ Printed: ONE JSON line with the step throughput (attention TFLOP/s), the
 CLiS kernel alone, the online-softmax baseline and its lazy-rescale form
 (FlashAttention-4's conditional rescaling), the speedups, the roofline
 of the dominant kernel (the fixed-stabilizer attention kernel; per-launch
-durations from HIP events on the stream the library launches on), the rate
-of an MFMA-only probe on the same GPU, the fp64 CPU oracle timed on a
+durations from HIP events on the stream the library launches on), the rates
+of an MFMA-only probe on the same GPU (constant and random operands), the
+fp64 CPU oracle timed on a
 bounded sample of the same workload, and the step's output checked against
 that oracle sample (and every head's certification flag against the
 oracle's).
@@ -88,24 +89,27 @@ def measured_traffic(kernel: str, source: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def mfma_probe(device, iters: int = 40000, blocks: int = 2048, reps: int = 5):
+def mfma_probe(device, random: bool, iters: int = 40000, blocks: int = 2048, reps: int = 5):
     """Rate (TFLOP/s) of an MFMA-only loop of the attention kernels' MFMA
-    (libclis_probe.so), about 25 ms per call: the sustained matrix-core rate
-    of this GPU, as a measured ceiling beside the published peak."""
+    (libclis_probe.so), 18-25 ms per call.  With constant operands it runs at
+    the chip's top clock, near the published peak; with random operands that
+    differ from one MFMA to the next the power limit lowers the clock, and
+    that rate is the ceiling a kernel whose operands keep changing can reach."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "softmax_stabilization_video_amd", "libclis_probe.so")
     if not os.path.exists(path):
         return None
     L = ctypes.CDLL(path)
-    L.clis_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.clis_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     L.clis_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     L.clis_probe_mfma_flops.restype = ctypes.c_double
     out = torch.empty(blocks * 256, dtype=torch.float32, device=device)
     stream = torch.cuda.current_stream()
 
     def call():
-        r = L.clis_probe_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters, ctypes.c_void_p(stream.cuda_stream))
+        r = L.clis_probe_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters, int(random),
+                              ctypes.c_void_p(stream.cuda_stream))
         if r != 0:
             raise RuntimeError(f"clis_probe_mfma failed: {r}")
     for _ in range(2):
@@ -397,10 +401,13 @@ def main(argv=None):
             "algorithmic_flops_per_launch": flops, "launch_ms_mean": round(ms, 4),
         }
     if w.dtype == "bf16" and args.only == "all":
-        probe = mfma_probe(q.device)
+        probe = mfma_probe(q.device, random=False)
         if probe:
             out["mfma_probe_tflops"] = round(probe, 1)
             out["pct_measured_mfma_peak"] = round(100 * value / probe, 2)
+            probe_rnd = mfma_probe(q.device, random=True)
+            out["mfma_probe_random_tflops"] = round(probe_rnd, 1)
+            out["pct_random_operand_mfma_ceiling"] = round(100 * value / probe_rnd, 2)
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample")
         out["cpu_baseline"], sample = cpu_baseline(w, Q, K, V, args.cpu_budget)

@@ -92,6 +92,11 @@ attn_fwd_fp32(const float* __restrict__ Q, const float* __restrict__ K, const fl
               float* __restrict__ O, const float* __restrict__ mu, const int32_t* __restrict__ cert,
               int32_t* __restrict__ route_out, int Nq, int Nk, float c2, float* __restrict__ lse,
               float* __restrict__ o_acc, float* __restrict__ l_acc, int accumulate, int kv_offset) {
+  // No implicit fusing of a product into a following add: each route computes
+  // the operations as written (explicit fmaf where one rounding is meant), so
+  // its results do not depend on which other routes the instance can take --
+  // auto mode equals the forced route bitwise.
+#pragma clang fp contract(off)
   constexpr int NT = D / 32;   // 32-dim blocks of O^T
   constexpr int OST = D + 4;   // LDS row stride of a wave's partial O (floats)
   __shared__ __attribute__((aligned(16))) float part_o[kWaves][kRows][OST];

@@ -160,6 +160,60 @@ def test_mixed_routing_small(clis):
     run_attention(clis, w, host, dev, mu, cert)
 
 
+FP32_MIXED = [
+    # name, B, H, Nq, Nk, d, causal: short fp32 heads (one-launch certification),
+    # ragged and causal, and a longer one (split certification)
+    ("fp32_mixed_d64", 1, 8, 256, 256, 64, False),
+    ("fp32_mixed_d128_ragged", 2, 4, 77, 300, 128, False),
+    ("fp32_mixed_causal", 1, 3, 500, 500, 128, True),
+    ("fp32_mixed_16_heads", 1, 16, 512, 512, 64, False),
+    ("fp32_mixed_split_cert", 1, 4, 1500, 1500, 64, False),
+]
+
+
+@pytest.mark.parametrize("case", FP32_MIXED, ids=[c[0] for c in FP32_MIXED])
+def test_fp32_mixed_routing(clis, case):
+    """fp32 with both routes taken.  Every third head is made to fail
+    certification the way a conservative certificate does: key 0 becomes 200
+    times a channel in which every query is zero, so kappa (and B_h) exceed
+    the cap while every logit stays as it was (the new key's logit is exactly
+    0) and fp32 keeps its 1e-5 accuracy on the online route.  Routes equal
+    clis_certify's flags and the oracle's; every mode matches the oracle; auto
+    mode equals the forced route of each head bitwise (the fp32 kernel fuses
+    no product into an add by itself, so its online and fixed forms compute
+    the same operations in every route); and certifying inside the call gives
+    bitwise the outputs and log-sum-exps of a call given clis_certify's
+    certificate, in auto and in forced fixed mode."""
+    import torch
+    name, B, H, Nq, Nk, d, causal = case
+    w = workloads.custom(name, B, H, Nq, d, "fp32", causal, Nk=Nk)
+    Q, K, V = (a.copy() for a in workloads.make_inputs(w, 21))
+    fail = np.arange(B * H) % 3 == 1
+    for i in np.flatnonzero(fail):
+        b, h = divmod(int(i), H)
+        Q[b, h, :, 0] = 0.0
+        K[b, h, 0, :] = 0.0
+        K[b, h, 0, 0] = 200.0
+    host = (Q, K, V)
+    dev = tuple(to_device(a, "fp32") for a in host)
+    mu, cert, ref = check_certify(clis, w, host, dev)
+    assert np.array_equal(ref["cert"].ravel().astype(bool), ~fail)
+    run_attention(clis, w, host, dev, mu, cert)
+    say("certificate inside the call vs given", name)
+    o_in, route_in, lse_in = clis.clis_attn_fwd(*dev, w.scale, causal, mode="auto", want_route=True,
+                                                want_lse=True)
+    o_giv, route_giv, lse_giv = clis.clis_attn_fwd(*dev, w.scale, causal, mode="auto", mu=mu, cert=cert,
+                                                   want_route=True, want_lse=True)
+    f_in = clis.clis_attn_fwd(*dev, w.scale, causal, mode="fixed")
+    f_giv = clis.clis_attn_fwd(*dev, w.scale, causal, mode="fixed", mu=mu)
+    torch.cuda.synchronize()
+    assert torch.equal(route_in, cert) and torch.equal(route_giv, cert)
+    assert torch.equal(o_in, o_giv) and torch.equal(lse_in, lse_giv)
+    # forced fixed on the failing heads is not promised finite: compare with
+    # NaN and Inf mapped to numbers, so that their positions must agree too
+    assert torch.equal(torch.nan_to_num(f_in), torch.nan_to_num(f_giv))
+
+
 def test_caller_supplied_certificate_is_used(clis):
     """mu/cert passed in: same result as letting the call certify itself."""
     import torch

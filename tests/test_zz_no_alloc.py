@@ -28,6 +28,8 @@ CASES = [
     ("smaller", 1, 3, 700, 64, False, 22, "bf16"),
     ("smaller_causal", 1, 2, 500, 128, True, 23, "bf16"),
     ("fp32", 1, 4, 600, 64, False, 24, "fp32"),
+    # short fp32 heads: one-launch certification
+    ("fp32_short", 1, 4, 256, 64, False, 25, "fp32"),
 ]
 
 
