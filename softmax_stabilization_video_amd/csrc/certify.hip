@@ -299,9 +299,12 @@ __global__ void __launch_bounds__(kThreads)
 cert_norms(const T* __restrict__ Q, const T* __restrict__ K, const double* __restrict__ kbar,
            int Nq, int Nk, int Sk, int Sq, double c2, float* __restrict__ mu,
            double* __restrict__ kap_part, double* __restrict__ qss_part) {
-  // 1-D grid: any head count
-  norms_block<T, D>(Q, K, kbar, Nq, Nk, Sk, Sq, c2, mu, kap_part, qss_part, blockIdx.x / (Sk + Sq),
-                    blockIdx.x % (Sk + Sq));
+  // 1-D grid: any head count.  Heads in reverse order: the keys that
+  // cert_keys_values read last are the ones still cached (measured 2-3%
+  // faster than forward order on the long workloads; results do not depend
+  // on the order, each block writes its own partial).
+  const unsigned b = gridDim.x - 1 - blockIdx.x;
+  norms_block<T, D>(Q, K, kbar, Nq, Nk, Sk, Sq, c2, mu, kap_part, qss_part, b / (Sk + Sq), b % (Sk + Sq));
 }
 
 // ceil(log2 x) for finite x >= 1, exactly.
