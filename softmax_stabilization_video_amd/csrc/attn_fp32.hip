@@ -107,13 +107,16 @@ attn_fwd_fp32(const float* __restrict__ Q, const float* __restrict__ K, const fl
   const int bh = blockIdx.x / n_qt;
   // causal: the longest query tiles (most keys) first
   const int qt = CAUSAL ? n_qt - 1 - blockIdx.x % n_qt : blockIdx.x % n_qt;
-  const bool FIXED = ROUTE == kFixed || (ROUTE == kAuto && cert[bh] != 0);
-  if (route_out && blockIdx.x % n_qt == 0 && threadIdx.x == 0) route_out[bh] = FIXED ? 1 : 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, col = lane & 31;
   const int q0 = qt * kRows;
   const int qrow = q0 + col;  // this lane's query
   const bool qvalid = qrow < Nq;
+  // the row's stabilizer is read whenever the head may run fixed, before the
+  // flag is known, so that the two loads are in flight together
+  const float mu_row = (ROUTE != kOnline && qvalid) ? mu[(size_t)bh * Nq + qrow] : 0.f;
+  const bool FIXED = ROUTE == kFixed || (ROUTE == kAuto && cert[bh] != 0);
+  if (route_out && blockIdx.x % n_qt == 0 && threadIdx.x == 0) route_out[bh] = FIXED ? 1 : 0;
   const float* Kh = K + (size_t)bh * Nk * D;
   const float* Vh = V + (size_t)bh * Nk * D;
 
@@ -139,7 +142,7 @@ attn_fwd_fp32(const float* __restrict__ Q, const float* __restrict__ K, const fl
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
-  float m = FIXED ? (qvalid ? mu[(size_t)bh * Nq + qrow] : 0.f) : -INFINITY;
+  float m = FIXED ? mu_row : -INFINITY;
   float l = 0.f;  // this lane's 16 keys of every tile; the halves are added at the end
 
   // local keys this block needs (the causal mask compares global indices)
@@ -291,7 +294,7 @@ hipError_t launch_d(const AttnArgs& a, bool fixed, hipStream_t s) {
 
 hipError_t launch_attn_fp32(const AttnArgs& a, bool fixed, hipStream_t s) {
   if (a.head_list) return hipErrorInvalidValue;  // the fp32 kernel routes by itself
-  if (a.cert && !a.mu) return hipErrorInvalidValue;
+  if ((a.cert || fixed) && !a.mu) return hipErrorInvalidValue;  // the kernel reads mu on these routes
   if (a.d == 128) return launch_d<128>(a, fixed, s);
   if (a.d == 64) return launch_d<64>(a, fixed, s);
   return hipErrorInvalidValue;
