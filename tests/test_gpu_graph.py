@@ -2,8 +2,9 @@
 kernels on the caller's stream: no host synchronization, routing read on the
 device, work counters zeroed by a kernel (no memset node).  A captured auto-mode
 call (certification, routing, both attention kernels, the run-time work pool and
-the key-split combine) therefore replays to the eager result, bitwise, replay
-after replay, with other work and synchronizations on the stream in between.
+the key-split combine; for fp32 certification and the self-routing kernel)
+therefore replays to the eager result, bitwise, replay after replay, with other
+work and synchronizations on the stream in between.
 Key-shard calls (clis_attn_fwd_partial + clis_attn_combine) are captured too.
 """
 import pytest
@@ -38,12 +39,24 @@ def _capture(fn):
     return g
 
 
-def test_auto_mode_call_replays_bitwise(clis):
+GRAPH_CASES = [
+    # dtype, N, d: bf16 (certification kernels, routing, both attention kernels,
+    # the pools and the key-split combine); fp32 with one-launch certification
+    # (N <= 1024) and with the split certification kernels, each followed by
+    # the self-routing fp32 attention kernel
+    ("bf16", 3000, 128),
+    ("fp32", 700, 64),
+    ("fp32", 1500, 128),
+]
+
+
+@pytest.mark.parametrize("dtype,N,d", GRAPH_CASES, ids=[f"{c[0]}_{c[1]}_d{c[2]}" for c in GRAPH_CASES])
+def test_auto_mode_call_replays_bitwise(clis, dtype, N, d):
     import torch
-    # a third of the heads fail certification, so both kernels run; 12 query
-    # tiles per fixed head and 24 per online head give pools with whole items
-    # and, in the fixed kernel, key splits
-    w = workloads.custom("graph_auto", 1, 6, 3000, 128, "bf16", False, key_bias_std=2.0,
+    # a third of the heads fail certification, so both routes run; for bf16,
+    # 12 query tiles per fixed head and 24 per online head give pools with
+    # whole items and, in the fixed kernel, key splits
+    w = workloads.custom(f"graph_auto_{dtype}", 1, 6, N, d, dtype, False, key_bias_std=2.0,
                          fail_frac=0.34, fail_qk_scale=40.0)
     Q, K, V = workloads.make_inputs(w, 61)
     q, k, v = (to_device(a, w.dtype) for a in (Q, K, V))
