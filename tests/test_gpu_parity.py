@@ -131,6 +131,9 @@ SMALL = [
     ("fp32_tail_d128", 1, 2, 1000, 1000, 128, "fp32", False),
     ("fp32_causal", 1, 2, 700, 700, 128, "fp32", True),
     ("fp32_cross", 1, 2, 33, 517, 64, "fp32", False),
+    ("fp32_causal_d64", 1, 2, 333, 333, 64, "fp32", True),
+    ("fp32_one_key", 1, 2, 40, 1, 64, "fp32", False),
+    ("fp32_one_query", 1, 2, 1, 77, 128, "fp32", False),
     # medium tailed fp32 shapes: 4100 = 128 tiles of 32 keys and a 4-key tail
     ("fp32_4100_d64", 1, 2, 4100, 4100, 64, "fp32", False),
     ("fp32_4100_d128_causal", 1, 1, 4100, 4100, 128, "fp32", True),
