@@ -169,8 +169,16 @@ __device__ __forceinline__ void kbar_block_impl(const double* sums, int Nk, int 
   const int c = threadIdx.x;
   if (vmax_blk) {
     double m = 0.0;
-    if (c < D)
-      for (int i = c; i < nblk; i += D) m = max_keep_nan(m, (double)vmax_blk[i]);
+    if (c < D) {
+      // eight loads in flight per lane (a maximum does not depend on the order)
+      for (int i0 = c; i0 < nblk; i0 += 8 * D) {
+        float t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = i0 + u * D < nblk ? vmax_blk[i0 + u * D] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m = max_keep_nan(m, (double)t[u]);
+      }
+    }
     for (int off = 32; off > 0; off >>= 1) m = max_keep_nan(m, __shfl_xor(m, off));
     if (c < D && (c & 63) == 0) red[c >> 6] = m;
     __syncthreads();
@@ -183,7 +191,15 @@ __device__ __forceinline__ void kbar_block_impl(const double* sums, int Nk, int 
   if (c < D) {
     const double* p = sums + c;
     double s = 0.0;
-    for (int i = 0; i < Sk; ++i) s += p[(size_t)i * D];
+    int i = 0;
+    for (; i + 8 <= Sk; i += 8) {  // eight loads in flight, then the adds in split order
+      double t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = p[(size_t)(i + u) * D];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += t[u];
+    }
+    for (; i < Sk; ++i) s += p[(size_t)i * D];
     kbar[c] = s / (double)Nk;
     if (kbar_copy) kbar_copy[c] = s / (double)Nk;
   }
@@ -346,27 +362,30 @@ __device__ __forceinline__ void finalize_values(double vmax, double kap2, double
   stats[h] = st;
 }
 
-// The same from the split partials, maxima taken in split order.
-__device__ __forceinline__ void finalize_head(const double* __restrict__ vmax_part,
-                                              const double* __restrict__ kap_part,
-                                              const double* __restrict__ qss_part, int Nk, int Sk, int Sq,
-                                              double c2, int32_t* __restrict__ cert,
-                                              clis_head_stats_t* __restrict__ stats, int h) {
-  double vmax = 0.0, kap2 = 0.0, qss = 0.0;
-  for (int i = 0; i < Sk; ++i) {
-    vmax = max_keep_nan(vmax, vmax_part[(size_t)h * Sk + i]);
-    kap2 = max_keep_nan(kap2, kap_part[(size_t)h * Sk + i]);
-  }
-  for (int i = 0; i < Sq; ++i) qss = max_keep_nan(qss, qss_part[(size_t)h * Sq + i]);
-  finalize_values(vmax, kap2, qss, Nk, c2, cert, stats, h);
-}
+// The same from the split partials, one wave per head: lane i takes splits
+// i, i + 64, ... and the lanes' maxima meet by shuffles (a maximum does not
+// depend on the order, and a NaN is kept whichever lane holds it).
+constexpr int kFinalizeHeads = kThreads / 64;  // heads per block
 
 __global__ void __launch_bounds__(kThreads)
 cert_finalize(const double* __restrict__ vmax_part, const double* __restrict__ kap_part,
               const double* __restrict__ qss_part, int BH, int Nk, int Sk, int Sq, double c2,
               int32_t* __restrict__ cert, clis_head_stats_t* __restrict__ stats) {
-  for (int h = blockIdx.x * kThreads + threadIdx.x; h < BH; h += gridDim.x * kThreads)
-    finalize_head(vmax_part, kap_part, qss_part, Nk, Sk, Sq, c2, cert, stats, h);
+  const int lane = threadIdx.x & 63;
+  const long long h = (long long)blockIdx.x * kFinalizeHeads + threadIdx.x / 64;
+  if (h >= BH) return;  // whole waves
+  double vmax = 0.0, kap2 = 0.0, qss = 0.0;
+  for (int i = lane; i < Sk; i += 64) {
+    vmax = max_keep_nan(vmax, vmax_part[h * Sk + i]);
+    kap2 = max_keep_nan(kap2, kap_part[h * Sk + i]);
+  }
+  for (int i = lane; i < Sq; i += 64) qss = max_keep_nan(qss, qss_part[h * Sq + i]);
+  for (int off = 32; off > 0; off >>= 1) {
+    vmax = max_keep_nan(vmax, __shfl_xor(vmax, off));
+    kap2 = max_keep_nan(kap2, __shfl_xor(kap2, off));
+    qss = max_keep_nan(qss, __shfl_xor(qss, off));
+  }
+  if (lane == 0) finalize_values(vmax, kap2, qss, Nk, c2, cert, stats, (int)h);
 }
 
 // Shapes with one key split and one query split: the four passes for one
@@ -519,7 +538,7 @@ hipError_t certify_typed(const CertifyArgs& a, hipStream_t s) {
   cert_kbar<D><<<BH, D, 0, s>>>(a.ksum_part, a.Nk, Sk, a.kbar, a.vmax_blk, a.vmax_nblk, a.vmax_part);
   cert_norms<T, D><<<(unsigned)(BH * (Sk + Sq)), kThreads, 0, s>>>(q, k, a.kbar, a.Nq, a.Nk, Sk, Sq, c2, a.mu,
                                                                     a.kap_part, a.qss_part);
-  const int fb = (BH + kThreads - 1) / kThreads;
+  const int fb = (int)(((long long)BH + kFinalizeHeads - 1) / kFinalizeHeads);
   cert_finalize<<<fb, kThreads, 0, s>>>(a.vmax_part, a.kap_part, a.qss_part, BH, a.Nk, Sk, Sq, c2,
                                         a.cert, a.stats);
   return hipGetLastError();
