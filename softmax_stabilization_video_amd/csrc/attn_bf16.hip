@@ -797,24 +797,29 @@ attn_fwd_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
-// Finishes the pool's key splits: workgroup t sums the kMaxSplit parts of the
-// t-th split item (the last query tile of list slot t) in split order, then
+// Finishes the pool's key splits: the kMaxSplit parts of the t-th split item
+// (the last query tile of list slot t) are summed in split order, then
 // O = sum o / sum l (and the log-sum-exp when asked), for the rows that
-// exist.  256 threads: each handles 4 channels of one row per pass.
+// exist.  Workgroup t * (BM / kCombineRows) + c takes rows c * kCombineRows ...
+// of item t; 256 threads, each 4 channels of one row per pass.
+constexpr int kCombineRows = 32;
+
 template <int D, int BM>
 __global__ void __launch_bounds__(256)
 tail_combine(const float* __restrict__ tail_o, const float* __restrict__ tail_l, uint16_t* __restrict__ O,
              const float* __restrict__ mu, float* __restrict__ lse, const int32_t* __restrict__ head_list,
              const int32_t* __restrict__ split_heads, int n_slots, int Nq) {
   constexpr int GROUPS = D / 4, ROWS = 256 / GROUPS;  // rows per pass
+  constexpr int CHUNKS = BM / kCombineRows;
+  static_assert(BM % kCombineRows == 0 && kCombineRows % ROWS == 0, "whole passes per chunk");
   const int n_qt = (Nq + BM - 1) / BM;
   const int S = split_heads ? *split_heads : head_list ? 0 : min(n_slots, kSplitHeads);
-  const int t = blockIdx.x;
+  const int t = blockIdx.x / CHUNKS, chunk = blockIdx.x % CHUNKS;
   if (t >= S) return;
   const int slot = t, qt = n_qt - 1;
   const int bh = head_list ? head_list[slot] : slot;
   const int cg = threadIdx.x % GROUPS, r0 = threadIdx.x / GROUPS;
-  for (int r = r0; r < BM; r += ROWS) {
+  for (int r = chunk * kCombineRows + r0; r < (chunk + 1) * kCombineRows; r += ROWS) {
     const int qrow = qt * BM + r;
     if (qrow >= Nq) break;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -882,10 +887,10 @@ hipError_t launch_t(const AttnArgs& a, const uint16_t* vt, int nk_pad, hipStream
       a.mu, a.head_list, a.head_count, a.n_slots, a.Nq, a.Nk, nk_pad, a.c2, a.lse, a.o_acc, a.l_acc,
       a.accumulate, a.kv_offset, a.tail_o, a.tail_l, conc, conc > 0 ? a.sched : nullptr, a.split_heads);
   if constexpr (TAIL) {
-    if (conc > 0 && splits) {  // one workgroup per possible split item
+    if (conc > 0 && splits) {  // workgroups for every row chunk of every possible split item
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      tail_combine<D, G::BM><<<(unsigned)kSplitHeads, 256, 0, s>>>(
+      tail_combine<D, G::BM><<<(unsigned)(kSplitHeads * (G::BM / kCombineRows)), 256, 0, s>>>(
           a.tail_o, a.tail_l, static_cast<uint16_t*>(a.o), a.mu, a.lse, a.head_list, a.split_heads, a.n_slots,
           a.Nq);
     }
